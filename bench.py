@@ -1,0 +1,217 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused shared + routed MoE layer on one MI355X.
+
+One step = one pass of the whole layer (route + shared append, align/sort/pad,
+the fused FP8 expert FFN over all 9 slots, weighted combine) over one batch of
+synthetic input already resident in HBM. The default workload is the TP8
+decode shard: T=64 tokens, H=5120, 160 routed + 1 shared experts, I=192,
+top-8 + shared. Two independent weight sets (2 x 475 MB) are cycled so the
+weights stream from HBM rather than from the 256 MB last-level cache.
+
+Prints one JSON line (see README/DESIGN for the fields). `--gpus` above 1 is
+refused: this build measures one GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+FP8_PEAK_TFLOPS = 5000.0       # MI355X dense fp8 MFMA (no sparsity)
+
+WORKLOAD_TEXT = {
+    "decode": "GLM4-MoE TP8 shard, decode: T=64 tokens, H=5120, 160 routed + 1 shared SwiGLU experts, "
+              "I=192, top-8 + shared = 9 slots, fp8 e4m3 weights with per-output-channel fp32 scales",
+    "prefill": "GLM4-MoE TP8 shard, prefill chunk: T=4096 tokens, H=5120, 160 routed + 1 shared, I=192, "
+               "top-8 + shared, per-channel fp8 e4m3 weights",
+    "prefill16k_zipf": "GLM4-MoE TP8 shard, 16384-token chunked-prefill batch with Zipf(1.1)-skewed routing",
+    "unsharded_block": "unsharded expert width: T=4096, H=5120, 160+1 experts, I=1536, top-8 + shared, "
+                       "fp8 e4m3 weights with 128x128 block scales",
+}
+DEFAULT_BLOCK_M = {"decode": 16, "prefill": 64, "prefill16k_zipf": 128, "unsharded_block": 64, "tiny": 16}
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def copy_calibration(mib: int, reps: int):
+    """A plain device copy of known size, for scaling the FETCH_SIZE / WRITE_SIZE counters."""
+    import torch
+    n = mib * (1 << 20)
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_read": n, "bytes_written": n, "reps": reps}), flush=True)
+
+
+def cpu_baseline(inp, budget_s: float):
+    """The CPU oracle (fused form, as it stands) on a bounded token sample."""
+    import numpy as np
+    import oracle
+    from workloads import f32_from_bf16_bits
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([d.get("num_threads", 1) for d in threadpool_info() if d.get("user_api") == "blas"] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count()
+    c = inp.cfg
+    x = f32_from_bf16_bits(inp.x_bf16)
+    n = min(c.T, 64)
+    times = []
+    t_all = time.perf_counter()
+    # at least 3 runs and about 10 s of work, within the budget
+    while len(times) < 3 or (sum(times) < 10.0 and len(times) < 15 and
+                             (time.perf_counter() - t_all) < budget_s):
+        tok = np.arange(n)
+        t0 = time.perf_counter()
+        oracle.moe_fused(x, inp.logits, c.K, inp.w13_q, inp.s13, inp.w2_q, inp.s2, tokens=tok)
+        times.append(time.perf_counter() - t0)
+    med = statistics.median(times)
+    return {"value": n / med, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"first {n} tokens of the {c.name} batch (routing over all {c.T}), float64 numpy "
+                      f"oracle, median of {len(times)} runs ({med:.2f} s each)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="decode", choices=sorted(WORKLOAD_TEXT))
+    ap.add_argument("--block-m", type=int, default=None)
+    ap.add_argument("--weight-sets", type=int, default=2)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=30.0)
+    ap.add_argument("--copy-calib-mib", type=int, default=0,
+                    help="only run a plain copy of this many MiB (counter calibration) and exit")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(see DESIGN.md, 'How the path would shard').", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    from workloads import CONFIGS, generate
+    from shared_routed_expert_amd import FusedMoE, DeviceWeights
+
+    if args.copy_calib_mib:
+        copy_calibration(args.copy_calib_mib, max(args.steps, 1))
+        return
+
+    cfg = CONFIGS[args.workload]
+    bm = args.block_m or DEFAULT_BLOCK_M[args.workload]
+    dev = "cuda:0"
+    log(f"bench: generating {args.workload} inputs ({args.weight_sets} weight sets)")
+    sets = [generate(cfg, weight_set=j) for j in range(args.weight_sets)]
+    inp = sets[0]
+    weights = [DeviceWeights.from_numpy(s.w13_q, s.s13, s.w2_q, s.s2, device=dev) for s in sets]
+    for s in sets[1:]:
+        s.w13_q = s.w2_q = None
+    x = torch.from_numpy(inp.x_bf16.view(np.int16)).to(dev).view(torch.bfloat16)
+    logits = torch.from_numpy(inp.logits).to(dev)
+    layer = FusedMoE(cfg.T, cfg.H, cfg.I, cfg.E, cfg.K, bm, weights[0].scale_mode, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        layer.forward(x, logits, weights[i % len(weights)], 1.0, stream)
+
+    log(f"bench: warmup {args.warmup} steps")
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # Timed region 1: the whole layer, K steps.
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for i in range(args.steps):
+        step(i)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = ev0.elapsed_time(ev1) / args.steps
+    log(f"bench: {ms_per_step * 1e3:.1f} us/step (wall {wall * 1e3 / args.steps:.1f} us/step)")
+
+    # Timed region 2: the same steps with HIP events between the stages (same stream),
+    # giving each stage's average duration, the dominant kernel's included.
+    names = ["route", "align", "quant_x", "gate_up", "down", "combine"]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        e = evs[i]
+        W = weights[i % len(weights)]
+        e[0].record(stream)
+        layer.route(logits, 1.0, stream)
+        e[1].record(stream)
+        layer.align(stream)
+        e[2].record(stream)
+        marks = iter(e[3:6])
+        layer.ffn_stages(x, W, stream, between=lambda _n: next(marks).record(stream))
+        layer.combine(stream)
+        e[6].record(stream)
+    torch.cuda.synchronize()
+    stage_us = {n: 1e3 * statistics.mean(evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(args.steps))
+                for j, n in enumerate(names)}
+
+    counts = layer.expert_counts.cpu().numpy()
+    active = int((counts > 0).sum())
+    T, H, I, E1, K1 = cfg.T, cfg.H, cfg.I, cfg.E1, cfg.K1
+    blk = cfg.scale_mode == "block128"
+    s13_bytes = (2 * I // 128) * (H // 128) * 4 if blk else 2 * I * 4
+    s2_bytes = (H // 128) * (I // 128) * 4 if blk else H * 4
+    # Algorithmic bytes of the gate_up kernel: each activated expert's W13 (2*I*H fp8) and its
+    # scales read once, plus the quantised activations x_q (T*H fp8) read once.
+    gate_up_bytes = active * (2 * I * H + s13_bytes) + T * H
+    gate_up_s = stage_us["gate_up"] * 1e-6
+    achieved = gate_up_bytes / gate_up_s / 1e9
+    layer_bytes = active * (3 * I * H + s13_bytes + s2_bytes) + T * H * 2 * 2 + T * cfg.E * 4 + T * K1 * 8
+    flops = T * K1 * 6 * H * I
+    step_s = ms_per_step * 1e-3
+
+    result = {
+        "metric": "fused MoE layer tokens/s + % fp8 MFMA peak (prefill) / % HBM BW (decode)",
+        "value": round(T / step_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8e4m3 (fp32 accumulate)",
+        "data": "synthetic (seeded; random-init fp8 expert weights of the GLM4-MoE TP8 shard shape)",
+        "config": {"workload": WORKLOAD_TEXT[args.workload], "T": T, "H": H, "I": I, "routed_experts": cfg.E,
+                   "shared_experts": 1, "top_k": cfg.K, "slots": K1, "block_m": bm,
+                   "weight_sets_cycled": len(weights), "active_experts": active, "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "kernel": "gate_up", "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": None, "alg_bytes_per_launch": gate_up_bytes,
+                     "avg_launch_us": round(stage_us["gate_up"], 2)},
+        "layer": {"alg_bytes": layer_bytes, "alg_GBps": round(layer_bytes / step_s / 1e9, 1),
+                  "hbm_frac": round(layer_bytes / step_s / 1e9 / HBM_PEAK_GBS, 4),
+                  "alg_TFLOPs": round(flops / step_s / 1e12, 2),
+                  "fp8_frac": round(flops / step_s / 1e12 / FP8_PEAK_TFLOPS, 4),
+                  "stage_us": {k: round(v, 2) for k, v in stage_us.items()}},
+    }
+    if not args.no_cpu_baseline:
+        log("bench: timing the CPU oracle")
+        result["cpu_baseline"] = cpu_baseline(inp, args.cpu_budget)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

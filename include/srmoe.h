@@ -1,0 +1,168 @@
+/*
+ * srmoe.h -- C ABI of the fused shared + routed MoE layer for AMD MI355X (gfx950).
+ *
+ * The layer (Optimizing GLM4-MoE for production, Novita AI, section 1 "Shared
+ * Experts Fusion"; intelliparadigm, GLM4-MoE production optimisation, section
+ * 2.1): every token goes through one shared expert and through the top-K of E
+ * routed experts chosen by its router, and the outputs are summed with the
+ * routing weights. The fusion treats the shared expert as one more routed
+ * expert (id E, the (E+1)-th), appends it to every token's routing table in
+ * the last slot (slot K, the 9th of 9 for K = 8) with coefficient 1.0, and runs
+ * all K+1 slots as one grouped expert-FFN pass:
+ *
+ *     out_t = sum_{k=0..K} w[t,k] * FFN_{ids[t,k]}(x_t),  ids[t,K] = E, w[t,K] = 1
+ *     FFN_e(v) = W2_e ( silu(Wgate_e v) * (Wup_e v) )      (SwiGLU)
+ *
+ * with FP8 E4M3 expert weights (the pages serve the model in FP8 at TP8, where
+ * the per-GPU expert intermediate size is 192).
+ *
+ * Conventions for every entry point below
+ *   - Pointers are DEVICE pointers unless marked "host". Arrays are row-major
+ *     and contiguous. bf16 values are passed as their uint16 bit patterns; FP8
+ *     values are OCP E4M3FN bytes (bias 7, max 448, no infinities).
+ *   - All work is enqueued asynchronously on `stream` (a hipStream_t; NULL is
+ *     the default stream). Buffers must stay alive until that work completes.
+ *     Nothing is synchronised and no device-to-host copy is made.
+ *   - The caller owns and allocates every buffer (including workspaces). The
+ *     library allocates no device memory, keeps no state between calls except
+ *     a thread-local copy of the last HIP error, and is reentrant.
+ *   - Argument checks run on the host before any launch. On failure a
+ *     negative srmoe_status is returned and no output is touched. A failed
+ *     launch returns SRMOE_ERR_HIP; srmoe_last_hip_error() gives the hipError_t.
+ *     Nothing throws, prints or aborts.
+ *   - T == 0 is valid everywhere. Route, FFN and combine then launch nothing;
+ *     align still writes its empty layout (all rows sentinel, counts 0).
+ *   - Inputs outside the contract (non-finite logits or activations, ids or
+ *     sort arrays not produced by this library) give undefined results.
+ *   - Pointers must be 16-byte aligned.
+ */
+#ifndef SRMOE_H_
+#define SRMOE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SRMOE_OK = 0,
+  SRMOE_ERR_INVALID_ARG = -1, /* null pointer, bad size, misaligned pointer    */
+  SRMOE_ERR_UNSUPPORTED = -2, /* a shape outside the supported set             */
+  SRMOE_ERR_WORKSPACE = -3,   /* workspace smaller than the *_workspace_bytes   */
+  SRMOE_ERR_HIP = -4          /* a HIP launch failed; see srmoe_last_hip_error() */
+} srmoe_status;
+
+typedef enum {
+  SRMOE_SCALE_PER_CHANNEL = 0, /* s13 [E1,2I], s2 [E1,H]; activations: one scale per row  */
+  SRMOE_SCALE_BLOCK128 = 1     /* s13 [E1,2I/128,H/128], s2 [E1,H/128,I/128]; activations:
+                                  one scale per row and 128-wide column group             */
+} srmoe_scale_mode;
+
+/* ---------------------------------------------------------------------------
+ * Step 1: router top-K plus the shared slot.
+ * Per token t: the K routed experts with the largest logits, ordered by
+ * (logit descending, expert id ascending) -- equal logits go to the lower id;
+ * weights w[t,k] = p_k / sum_{j in top-K} p_j with p = softmax(logits[t,0:E]);
+ * then slot K gets the shared expert: ids[t,K] = E, w[t,K] = shared_weight.
+ * (Shared expert as routed expert number E+1 in the last of K+1 positions:
+ * intelliparadigm section 2.1; Novita AI section 1. Softmax with renormalised
+ * top-K is the plainest router reading; the pages do not name it.)
+ *   logits   [T,E] float32 (router output for the E routed experts)
+ *   topk_ids [T,K+1] int32 out;  topk_w [T,K+1] float32 out
+ *   limits: 1 <= E <= 255, 0 <= K <= min(E,15).
+ * ------------------------------------------------------------------------- */
+int moe_route_topk_plus_shared(const float* logits, int T, int E, int K, float shared_weight,
+                               int32_t* topk_ids, float* topk_w, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Step 2: align / sort / pad the T*(K+1) (token, slot) entries by expert.
+ * Entry s = t*K1 + k has expert topk_ids[s]. Output, for experts in ascending
+ * id, the entries of each expert in ascending s (a stable counting sort),
+ * each expert's segment padded to a multiple of block_m with the sentinel
+ * T*K1 (an expert with no entries takes no rows), and the sentinel again up
+ * to P_max = moe_sorted_capacity(T,K1,E1,block_m).
+ *   topk_ids        [T*K1] int32 in, values in 0..E1-1
+ *   sorted_slot_ids [P_max] int32 out
+ *   block_expert    [P_max/block_m] int32 out: owning expert of rows
+ *                   b*block_m..(b+1)*block_m-1, or -1 past the used rows
+ *   expert_counts   [E1] int32 out: entries per expert
+ *   expert_offsets  [E1+1] int32 out: exclusive scan of the padded counts
+ *   num_padded      [1] int32 out: expert_offsets[E1]
+ *   workspace       >= moe_align_workspace_bytes(T,K1,E1) bytes, device
+ *   limits: 1 <= K1 <= 16, 1 <= E1 <= 256, block_m in {16,32,64,128}.
+ * Integer-only; results are deterministic and independent of scheduling.
+ * ------------------------------------------------------------------------- */
+int moe_align_by_expert(const int32_t* topk_ids, int T, int K1, int E1, int block_m,
+                        int32_t* sorted_slot_ids, int32_t* block_expert, int32_t* expert_counts,
+                        int32_t* expert_offsets, int32_t* num_padded, void* workspace,
+                        size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Step 3: the grouped SwiGLU expert FFN over all K+1 slots (one pass for the
+ * shared and the routed experts). For each sorted row with slot s = t*K1+k:
+ *   x_q      = FP8 absmax fake-quant of x[t] (scale amax/448, RNE, saturating;
+ *              per row, or per 128 group in block mode) -- activation step a3
+ *   g, u     = dequantised x_q against gate rows 0..I-1 / up rows I..2I-1 of
+ *              w13[e] (fp8 MFMA, fp32 accumulate, per-channel or per-block
+ *              scales)                                       -- step a4
+ *   a        = silu(g) * u (float32), FP8 absmax-quantised per row over I
+ *              (per 128 group in block mode)
+ *   y        = dequantised a against w2[e]                   -- step a5
+ *   slot_out[s,:] = bf16( topk_w[s] * y )   (kept in the workspace)
+ * Inputs:
+ *   x        [T,H] bf16;   w13 [E1,2I,H] e4m3;  w2 [E1,H,I] e4m3
+ *   s13, s2  float32 scales, shapes per scale_mode (see srmoe_scale_mode)
+ *   sorted_slot_ids, block_expert, num_padded: outputs of step 2 (same block_m)
+ *   topk_w   [T,K1] float32 routing weights (step 1)
+ *   workspace >= moe_ffn_workspace_bytes(...) bytes; also read by moe_combine
+ *   limits: H % 128 == 0; I % 32 == 0 (block mode: I % 128 == 0); E1 <= 256;
+ *           1 <= K1 <= 16; block_m in {16,32,64,128}.
+ * ------------------------------------------------------------------------- */
+int moe_fused_ffn(const uint16_t* x, const uint8_t* w13, const float* s13, const uint8_t* w2,
+                  const float* s2, int scale_mode, int T, int H, int I, int E1, int K1,
+                  int block_m, const int32_t* sorted_slot_ids, const int32_t* block_expert,
+                  const int32_t* num_padded, const float* topk_w, void* workspace,
+                  size_t ws_bytes, void* stream);
+
+/* The three stages of moe_fused_ffn, callable one at a time (same arguments,
+ * same workspace; call them in this order). moe_fused_ffn == all three. */
+int moe_ffn_quant_x(const uint16_t* x, int scale_mode, int T, int H, int I, int E1, int K1,
+                    int block_m, void* workspace, size_t ws_bytes, void* stream);
+int moe_ffn_gate_up(const uint8_t* w13, const float* s13, int scale_mode, int T, int H, int I,
+                    int E1, int K1, int block_m, const int32_t* sorted_slot_ids,
+                    const int32_t* block_expert, const int32_t* num_padded, void* workspace,
+                    size_t ws_bytes, void* stream);
+int moe_ffn_down(const uint8_t* w2, const float* s2, int scale_mode, int T, int H, int I, int E1,
+                 int K1, int block_m, const int32_t* sorted_slot_ids,
+                 const int32_t* block_expert, const int32_t* num_padded, const float* topk_w,
+                 void* workspace, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Step 4: weighted combine (Novita AI section 1: the experts' outputs are
+ * weighted and aggregated). out[t,:] = bf16( sum_{k=0..K1-1} slot_out[t*K1+k,:] )
+ * accumulated in float32 in slot order 0..K1-1, where slot_out (already scaled
+ * by the routing weights) is the one moe_fused_ffn left in `workspace`.
+ *   out [T,H] bf16 out.
+ * ------------------------------------------------------------------------- */
+int moe_combine(int T, int K1, int H, const void* workspace, size_t ws_bytes, uint16_t* out,
+                void* stream);
+
+/* Host helpers. */
+size_t moe_sorted_capacity(int T, int K1, int E1, int block_m); /* P_max, rows */
+size_t moe_align_workspace_bytes(int T, int K1, int E1);
+size_t moe_ffn_workspace_bytes(int T, int H, int I, int E1, int K1, int block_m, int scale_mode);
+/* Byte offsets inside the FFN workspace (host): out[0] slot_out [T*K1,H] bf16 (always 0),
+ * out[1] x_q [T,H] e4m3, out[2] x scales, out[3] a [P_max,I] float32 (sorted-row order),
+ * out[4] a_q [P_max,I] e4m3, out[5] a scales, out[6] total. For inspecting the stages;
+ * returns SRMOE_OK or SRMOE_ERR_INVALID_ARG / SRMOE_ERR_UNSUPPORTED for bad shapes. */
+int moe_ffn_workspace_offsets(int T, int H, int I, int E1, int K1, int block_m, int scale_mode,
+                              size_t* out /* host, 7 entries */);
+const char* srmoe_status_string(int status);
+int srmoe_last_hip_error(void); /* hipError_t of this thread's last failed launch, 0 if none */
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SRMOE_H_ */

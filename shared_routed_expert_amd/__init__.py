@@ -1,0 +1,23 @@
+"""Fused shared + routed MoE layer (GLM4-MoE Shared Experts Fusion) for AMD MI355X / gfx950.
+
+The compute lives in libsrmoe.so (hand-written HIP kernels behind a C ABI,
+declared in include/srmoe.h); this package is its thin ctypes binding plus
+buffer plumbing. Build the library with `python -m shared_routed_expert_amd.build`.
+The binding is loaded on first attribute access, so building never needs an
+already built library; using it without one raises ImportError.
+"""
+_BINDING = ("lib", "LIB_PATH", "SrmoeError", "SCALE_PER_CHANNEL", "SCALE_BLOCK128",
+            "moe_route_topk_plus_shared", "moe_align_by_expert", "moe_fused_ffn", "moe_ffn_quant_x",
+            "moe_ffn_gate_up", "moe_ffn_down", "moe_combine", "moe_sorted_capacity",
+            "moe_align_workspace_bytes", "moe_ffn_workspace_bytes", "moe_ffn_workspace_offsets")
+_LAYER = ("FusedMoE", "DeviceWeights")
+
+
+def __getattr__(name):
+    if name in _BINDING:
+        from . import _lib
+        return getattr(_lib, name)
+    if name in _LAYER:
+        from . import layer
+        return getattr(layer, name)
+    raise AttributeError(name)

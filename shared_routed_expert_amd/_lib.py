@@ -1,0 +1,155 @@
+"""ctypes binding of libsrmoe.so: argument marshalling only.
+
+Every function here has the name of the C entry point it calls and only turns
+torch tensors into device pointers (and the current torch stream into a
+hipStream_t). All computation happens in the library's HIP kernels. If the
+library has not been built the import fails loudly; there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libsrmoe.so")
+
+SRMOE_OK = 0
+SCALE_PER_CHANNEL = 0
+SCALE_BLOCK128 = 1
+
+
+class SrmoeError(RuntimeError):
+    def __init__(self, name, status, lib):
+        msg = lib.srmoe_status_string(status).decode()
+        hip = lib.srmoe_last_hip_error() if status == -4 else 0
+        super().__init__(f"{name} failed: {msg} (status {status}, hip error {hip})")
+        self.status = status
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with `python -m shared_routed_expert_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I, F, Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    sigs = {
+        "moe_route_topk_plus_shared": ([P, I, I, I, F, P, P, P], I),
+        "moe_align_by_expert": ([P, I, I, I, I, P, P, P, P, P, P, Z, P], I),
+        "moe_fused_ffn": ([P, P, P, P, P, I, I, I, I, I, I, I, P, P, P, P, P, Z, P], I),
+        "moe_ffn_quant_x": ([P, I, I, I, I, I, I, I, P, Z, P], I),
+        "moe_ffn_gate_up": ([P, P, I, I, I, I, I, I, I, P, P, P, P, Z, P], I),
+        "moe_ffn_down": ([P, P, I, I, I, I, I, I, I, P, P, P, P, P, Z, P], I),
+        "moe_combine": ([I, I, I, P, Z, P, P], I),
+        "moe_sorted_capacity": ([I, I, I, I], Z),
+        "moe_align_workspace_bytes": ([I, I, I], Z),
+        "moe_ffn_workspace_bytes": ([I, I, I, I, I, I, I], Z),
+        "moe_ffn_workspace_offsets": ([I, I, I, I, I, I, I, P], I),
+        "srmoe_status_string": ([I], ctypes.c_char_p),
+        "srmoe_last_hip_error": ([], I),
+    }
+    for name, (args, res) in sigs.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = res
+    return lib
+
+
+lib = _load()
+
+EXPORTED = ("moe_route_topk_plus_shared", "moe_align_by_expert", "moe_fused_ffn", "moe_ffn_quant_x",
+            "moe_ffn_gate_up", "moe_ffn_down", "moe_combine", "moe_sorted_capacity",
+            "moe_align_workspace_bytes", "moe_ffn_workspace_bytes", "moe_ffn_workspace_offsets",
+            "srmoe_status_string",
+            "srmoe_last_hip_error")
+
+
+def _ptr(t):
+    """Device pointer of a tensor, or an int / None passed through (raw pointers in tests)."""
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(name, status):
+    if status != SRMOE_OK:
+        raise SrmoeError(name, status, lib)
+    return status
+
+
+def moe_sorted_capacity(T, K1, E1, block_m):
+    return lib.moe_sorted_capacity(T, K1, E1, block_m)
+
+
+def moe_align_workspace_bytes(T, K1, E1):
+    return lib.moe_align_workspace_bytes(T, K1, E1)
+
+
+def moe_ffn_workspace_bytes(T, H, I, E1, K1, block_m, scale_mode):
+    return lib.moe_ffn_workspace_bytes(T, H, I, E1, K1, block_m, scale_mode)
+
+
+def moe_ffn_workspace_offsets(T, H, I, E1, K1, block_m, scale_mode):
+    """Returns a dict of byte offsets: slot_out, xq, sx, a, aq, sa, total."""
+    arr = (ctypes.c_size_t * 7)()
+    _check("moe_ffn_workspace_offsets",
+           lib.moe_ffn_workspace_offsets(T, H, I, E1, K1, block_m, scale_mode, arr))
+    return dict(zip(("slot_out", "xq", "sx", "a", "aq", "sa", "total"), list(arr)))
+
+
+def moe_route_topk_plus_shared(logits, T, E, K, shared_weight, topk_ids, topk_w, stream=None, check=True):
+    st = lib.moe_route_topk_plus_shared(_ptr(logits), T, E, K, shared_weight, _ptr(topk_ids),
+                                        _ptr(topk_w), _stream(stream))
+    return _check("moe_route_topk_plus_shared", st) if check else st
+
+
+def moe_align_by_expert(topk_ids, T, K1, E1, block_m, sorted_slot_ids, block_expert, expert_counts,
+                        expert_offsets, num_padded, workspace, ws_bytes, stream=None, check=True):
+    st = lib.moe_align_by_expert(_ptr(topk_ids), T, K1, E1, block_m, _ptr(sorted_slot_ids),
+                                 _ptr(block_expert), _ptr(expert_counts), _ptr(expert_offsets),
+                                 _ptr(num_padded), _ptr(workspace), ws_bytes, _stream(stream))
+    return _check("moe_align_by_expert", st) if check else st
+
+
+def moe_fused_ffn(x, w13, s13, w2, s2, scale_mode, T, H, I, E1, K1, block_m, sorted_slot_ids,
+                  block_expert, num_padded, topk_w, workspace, ws_bytes, stream=None, check=True):
+    st = lib.moe_fused_ffn(_ptr(x), _ptr(w13), _ptr(s13), _ptr(w2), _ptr(s2), scale_mode, T, H, I, E1,
+                           K1, block_m, _ptr(sorted_slot_ids), _ptr(block_expert), _ptr(num_padded),
+                           _ptr(topk_w), _ptr(workspace), ws_bytes, _stream(stream))
+    return _check("moe_fused_ffn", st) if check else st
+
+
+def moe_ffn_quant_x(x, scale_mode, T, H, I, E1, K1, block_m, workspace, ws_bytes, stream=None, check=True):
+    st = lib.moe_ffn_quant_x(_ptr(x), scale_mode, T, H, I, E1, K1, block_m, _ptr(workspace), ws_bytes,
+                             _stream(stream))
+    return _check("moe_ffn_quant_x", st) if check else st
+
+
+def moe_ffn_gate_up(w13, s13, scale_mode, T, H, I, E1, K1, block_m, sorted_slot_ids, block_expert,
+                    num_padded, workspace, ws_bytes, stream=None, check=True):
+    st = lib.moe_ffn_gate_up(_ptr(w13), _ptr(s13), scale_mode, T, H, I, E1, K1, block_m,
+                             _ptr(sorted_slot_ids), _ptr(block_expert), _ptr(num_padded),
+                             _ptr(workspace), ws_bytes, _stream(stream))
+    return _check("moe_ffn_gate_up", st) if check else st
+
+
+def moe_ffn_down(w2, s2, scale_mode, T, H, I, E1, K1, block_m, sorted_slot_ids, block_expert,
+                 num_padded, topk_w, workspace, ws_bytes, stream=None, check=True):
+    st = lib.moe_ffn_down(_ptr(w2), _ptr(s2), scale_mode, T, H, I, E1, K1, block_m,
+                          _ptr(sorted_slot_ids), _ptr(block_expert), _ptr(num_padded), _ptr(topk_w),
+                          _ptr(workspace), ws_bytes, _stream(stream))
+    return _check("moe_ffn_down", st) if check else st
+
+
+def moe_combine(T, K1, H, workspace, ws_bytes, out, stream=None, check=True):
+    st = lib.moe_combine(T, K1, H, _ptr(workspace), ws_bytes, _ptr(out), _stream(stream))
+    return _check("moe_combine", st) if check else st

@@ -1,0 +1,255 @@
+// C ABI of the fused shared + routed MoE layer: argument checks, workspace
+// layout and kernel launches on the caller's stream. See include/srmoe.h.
+#include "srmoe.h"
+
+#include "common.hpp"
+
+namespace srmoe {
+hipError_t launch_route(const float*, int, int, int, float, int32_t*, float*, hipStream_t);
+size_t align_workspace_bytes(int T, int K1, int E1);
+hipError_t launch_align(const int32_t*, int, int, int, int, int32_t*, int32_t*, int32_t*, int32_t*,
+                        int32_t*, void*, hipStream_t);
+hipError_t launch_quant_x(const uint16_t*, int, int, bool, uint8_t*, float*, hipStream_t);
+hipError_t launch_quant_a(const float*, int, int, bool, const int32_t*, uint8_t*, float*, hipStream_t);
+hipError_t launch_gate_up(const uint8_t*, const float*, const uint8_t*, const float*, bool,
+                          const int32_t*, const int32_t*, const int32_t*, float*, int, int, int, int,
+                          int, int, hipStream_t);
+hipError_t launch_down(const uint8_t*, const float*, const uint8_t*, const float*, bool,
+                       const int32_t*, const int32_t*, const int32_t*, const float*, uint16_t*, int,
+                       int, int, int, int, int, hipStream_t);
+hipError_t launch_combine(const uint16_t*, int, int, int, uint16_t*, hipStream_t);
+}  // namespace srmoe
+
+using namespace srmoe;
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+constexpr int kMaxT = 1 << 20;
+
+inline size_t al256(size_t n) { return (n + 255) / 256 * 256; }
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+inline hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
+
+int hip_status(hipError_t e) {
+  if (e == hipSuccess) return SRMOE_OK;
+  g_last_hip_error = (int)e;
+  return SRMOE_ERR_HIP;
+}
+
+// FFN workspace: slot_out first (moe_combine reads it at offset 0), then the
+// quantised activations, the SwiGLU product in float32 and its quantised copy.
+struct FfnLayout {
+  size_t slot_out, xq, sx, a, aq, sa, total;
+};
+
+FfnLayout ffn_layout(int T, int H, int I, int E1, int K1, int block_m, int mode) {
+  const size_t P = sorted_capacity(T, K1, E1, block_m);
+  const size_t gh = mode == SRMOE_SCALE_BLOCK128 ? (size_t)H / kGroup : 1;
+  const size_t gi = mode == SRMOE_SCALE_BLOCK128 ? (size_t)I / kGroup : 1;
+  FfnLayout L{};
+  size_t off = 0;
+  L.slot_out = off; off += al256((size_t)T * K1 * H * 2);
+  L.xq = off;       off += al256((size_t)T * H);
+  L.sx = off;       off += al256((size_t)T * gh * 4);
+  L.a = off;        off += al256(P * I * 4);
+  L.aq = off;       off += al256(P * I);
+  L.sa = off;       off += al256(P * gi * 4);
+  L.total = off;
+  return L;
+}
+
+bool valid_block_m(int bm) { return bm == 16 || bm == 32 || bm == 64 || bm == 128; }
+
+// Shape checks shared by the FFN entry points; 0 if fine.
+int check_ffn_dims(int scale_mode, int T, int H, int I, int E1, int K1, int block_m) {
+  if (T < 0 || T > kMaxT || H <= 0 || I <= 0 || E1 < 1 || K1 < 1) return SRMOE_ERR_INVALID_ARG;
+  if (scale_mode != SRMOE_SCALE_PER_CHANNEL && scale_mode != SRMOE_SCALE_BLOCK128)
+    return SRMOE_ERR_INVALID_ARG;
+  if (E1 > 256 || K1 > 16 || K1 > E1) return SRMOE_ERR_UNSUPPORTED;
+  if (!valid_block_m(block_m)) return SRMOE_ERR_UNSUPPORTED;
+  if (H % 128 != 0 || I % 32 != 0) return SRMOE_ERR_UNSUPPORTED;
+  if (scale_mode == SRMOE_SCALE_BLOCK128 && I % 128 != 0) return SRMOE_ERR_UNSUPPORTED;
+  if (H > 65536 || I > 16384) return SRMOE_ERR_UNSUPPORTED;
+  if ((size_t)T * K1 * H >= ((size_t)1 << 31)) return SRMOE_ERR_UNSUPPORTED;
+  return SRMOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t moe_sorted_capacity(int T, int K1, int E1, int block_m) {
+  if (T < 0 || K1 < 1 || E1 < 1 || !valid_block_m(block_m)) return 0;
+  return sorted_capacity(T, K1, E1, block_m);
+}
+
+size_t moe_align_workspace_bytes(int T, int K1, int E1) {
+  if (T < 0 || K1 < 1 || E1 < 1) return 0;
+  const size_t n = align_workspace_bytes(T, K1, E1);
+  return n > 256 ? n : 256;
+}
+
+size_t moe_ffn_workspace_bytes(int T, int H, int I, int E1, int K1, int block_m, int scale_mode) {
+  if (check_ffn_dims(scale_mode, T, H, I, E1, K1, block_m) != SRMOE_OK) return 0;
+  return ffn_layout(T, H, I, E1, K1, block_m, scale_mode).total;
+}
+
+int moe_ffn_workspace_offsets(int T, int H, int I, int E1, int K1, int block_m, int scale_mode,
+                              size_t* out) {
+  const int st = check_ffn_dims(scale_mode, T, H, I, E1, K1, block_m);
+  if (st != SRMOE_OK) return st;
+  if (!out) return SRMOE_ERR_INVALID_ARG;
+  const FfnLayout L = ffn_layout(T, H, I, E1, K1, block_m, scale_mode);
+  out[0] = L.slot_out; out[1] = L.xq; out[2] = L.sx; out[3] = L.a; out[4] = L.aq; out[5] = L.sa;
+  out[6] = L.total;
+  return SRMOE_OK;
+}
+
+const char* srmoe_status_string(int status) {
+  switch (status) {
+    case SRMOE_OK: return "ok";
+    case SRMOE_ERR_INVALID_ARG: return "invalid argument";
+    case SRMOE_ERR_UNSUPPORTED: return "unsupported shape";
+    case SRMOE_ERR_WORKSPACE: return "workspace too small";
+    case SRMOE_ERR_HIP: return "HIP launch failed (see srmoe_last_hip_error)";
+    default: return "unknown status";
+  }
+}
+
+int srmoe_last_hip_error(void) { return g_last_hip_error; }
+
+int moe_route_topk_plus_shared(const float* logits, int T, int E, int K, float shared_weight,
+                               int32_t* topk_ids, float* topk_w, void* stream) {
+  if (T < 0 || T > kMaxT || E < 1 || K < 0) return SRMOE_ERR_INVALID_ARG;
+  if (E > 255 || K > E || K > 15) return SRMOE_ERR_UNSUPPORTED;
+  if (T == 0) return SRMOE_OK;
+  if (!logits || !topk_ids || !topk_w) return SRMOE_ERR_INVALID_ARG;
+  if (!aligned16(logits) || !aligned16(topk_ids) || !aligned16(topk_w)) return SRMOE_ERR_INVALID_ARG;
+  return hip_status(launch_route(logits, T, E, K, shared_weight, topk_ids, topk_w, as_stream(stream)));
+}
+
+int moe_align_by_expert(const int32_t* topk_ids, int T, int K1, int E1, int block_m,
+                        int32_t* sorted_slot_ids, int32_t* block_expert, int32_t* expert_counts,
+                        int32_t* expert_offsets, int32_t* num_padded, void* workspace,
+                        size_t ws_bytes, void* stream) {
+  if (T < 0 || T > kMaxT || K1 < 1 || E1 < 1) return SRMOE_ERR_INVALID_ARG;
+  if (K1 > 16 || E1 > 256 || !valid_block_m(block_m)) return SRMOE_ERR_UNSUPPORTED;
+  if ((T > 0 && !topk_ids) || !sorted_slot_ids || !block_expert || !expert_counts ||
+      !expert_offsets || !num_padded || !workspace)
+    return SRMOE_ERR_INVALID_ARG;
+  if (!aligned16(topk_ids) || !aligned16(sorted_slot_ids) || !aligned16(block_expert) ||
+      !aligned16(expert_counts) || !aligned16(expert_offsets) || !aligned16(num_padded) ||
+      !aligned16(workspace))
+    return SRMOE_ERR_INVALID_ARG;
+  if (ws_bytes < moe_align_workspace_bytes(T, K1, E1)) return SRMOE_ERR_WORKSPACE;
+  // T == 0 still defines the (empty) layout: counts and offsets 0, all rows sentinel.
+  return hip_status(launch_align(topk_ids, T, K1, E1, block_m, sorted_slot_ids, block_expert,
+                                 expert_counts, expert_offsets, num_padded, workspace,
+                                 as_stream(stream)));
+}
+
+int moe_ffn_quant_x(const uint16_t* x, int scale_mode, int T, int H, int I, int E1, int K1,
+                    int block_m, void* workspace, size_t ws_bytes, void* stream) {
+  int st = check_ffn_dims(scale_mode, T, H, I, E1, K1, block_m);
+  if (st != SRMOE_OK) return st;
+  if (T == 0) return SRMOE_OK;
+  if (!x || !workspace || !aligned16(x) || !aligned16(workspace)) return SRMOE_ERR_INVALID_ARG;
+  const FfnLayout L = ffn_layout(T, H, I, E1, K1, block_m, scale_mode);
+  if (ws_bytes < L.total) return SRMOE_ERR_WORKSPACE;
+  char* ws = static_cast<char*>(workspace);
+  return hip_status(launch_quant_x(x, T, H, scale_mode == SRMOE_SCALE_BLOCK128,
+                                   reinterpret_cast<uint8_t*>(ws + L.xq),
+                                   reinterpret_cast<float*>(ws + L.sx), as_stream(stream)));
+}
+
+int moe_ffn_gate_up(const uint8_t* w13, const float* s13, int scale_mode, int T, int H, int I,
+                    int E1, int K1, int block_m, const int32_t* sorted_slot_ids,
+                    const int32_t* block_expert, const int32_t* num_padded, void* workspace,
+                    size_t ws_bytes, void* stream) {
+  int st = check_ffn_dims(scale_mode, T, H, I, E1, K1, block_m);
+  if (st != SRMOE_OK) return st;
+  if (T == 0) return SRMOE_OK;
+  if (!w13 || !s13 || !sorted_slot_ids || !block_expert || !num_padded || !workspace)
+    return SRMOE_ERR_INVALID_ARG;
+  if (!aligned16(w13) || !aligned16(s13) || !aligned16(sorted_slot_ids) || !aligned16(block_expert) ||
+      !aligned16(num_padded) || !aligned16(workspace))
+    return SRMOE_ERR_INVALID_ARG;
+  const FfnLayout L = ffn_layout(T, H, I, E1, K1, block_m, scale_mode);
+  if (ws_bytes < L.total) return SRMOE_ERR_WORKSPACE;
+  char* ws = static_cast<char*>(workspace);
+  const bool blk = scale_mode == SRMOE_SCALE_BLOCK128;
+  return hip_status(launch_gate_up(reinterpret_cast<const uint8_t*>(ws + L.xq),
+                                   reinterpret_cast<const float*>(ws + L.sx), w13, s13, blk,
+                                   sorted_slot_ids, block_expert, num_padded,
+                                   reinterpret_cast<float*>(ws + L.a), T, H, I, E1, K1, block_m,
+                                   as_stream(stream)));
+}
+
+int moe_ffn_down(const uint8_t* w2, const float* s2, int scale_mode, int T, int H, int I, int E1,
+                 int K1, int block_m, const int32_t* sorted_slot_ids, const int32_t* block_expert,
+                 const int32_t* num_padded, const float* topk_w, void* workspace, size_t ws_bytes,
+                 void* stream) {
+  int st = check_ffn_dims(scale_mode, T, H, I, E1, K1, block_m);
+  if (st != SRMOE_OK) return st;
+  if (T == 0) return SRMOE_OK;
+  if (!w2 || !s2 || !sorted_slot_ids || !block_expert || !num_padded || !topk_w || !workspace)
+    return SRMOE_ERR_INVALID_ARG;
+  if (!aligned16(w2) || !aligned16(s2) || !aligned16(sorted_slot_ids) || !aligned16(block_expert) ||
+      !aligned16(num_padded) || !aligned16(topk_w) || !aligned16(workspace))
+    return SRMOE_ERR_INVALID_ARG;
+  const FfnLayout L = ffn_layout(T, H, I, E1, K1, block_m, scale_mode);
+  if (ws_bytes < L.total) return SRMOE_ERR_WORKSPACE;
+  char* ws = static_cast<char*>(workspace);
+  const bool blk = scale_mode == SRMOE_SCALE_BLOCK128;
+  const int P_max = (int)sorted_capacity(T, K1, E1, block_m);
+  hipError_t e = launch_quant_a(reinterpret_cast<const float*>(ws + L.a), P_max, I, blk, num_padded,
+                                reinterpret_cast<uint8_t*>(ws + L.aq),
+                                reinterpret_cast<float*>(ws + L.sa), as_stream(stream));
+  if (e != hipSuccess) return hip_status(e);
+  return hip_status(launch_down(reinterpret_cast<const uint8_t*>(ws + L.aq),
+                                reinterpret_cast<const float*>(ws + L.sa), w2, s2, blk,
+                                sorted_slot_ids, block_expert, num_padded, topk_w,
+                                reinterpret_cast<uint16_t*>(ws + L.slot_out), T, H, I, E1, K1,
+                                block_m, as_stream(stream)));
+}
+
+int moe_fused_ffn(const uint16_t* x, const uint8_t* w13, const float* s13, const uint8_t* w2,
+                  const float* s2, int scale_mode, int T, int H, int I, int E1, int K1,
+                  int block_m, const int32_t* sorted_slot_ids, const int32_t* block_expert,
+                  const int32_t* num_padded, const float* topk_w, void* workspace,
+                  size_t ws_bytes, void* stream) {
+  int st = check_ffn_dims(scale_mode, T, H, I, E1, K1, block_m);
+  if (st != SRMOE_OK) return st;
+  if (T == 0) return SRMOE_OK;
+  // all pointer checks up front so that a bad call launches nothing
+  if (!x || !w13 || !s13 || !w2 || !s2 || !sorted_slot_ids || !block_expert || !num_padded ||
+      !topk_w || !workspace)
+    return SRMOE_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(w13) || !aligned16(s13) || !aligned16(w2) || !aligned16(s2) ||
+      !aligned16(sorted_slot_ids) || !aligned16(block_expert) || !aligned16(num_padded) ||
+      !aligned16(topk_w) || !aligned16(workspace))
+    return SRMOE_ERR_INVALID_ARG;
+  if (ws_bytes < ffn_layout(T, H, I, E1, K1, block_m, scale_mode).total) return SRMOE_ERR_WORKSPACE;
+  st = moe_ffn_quant_x(x, scale_mode, T, H, I, E1, K1, block_m, workspace, ws_bytes, stream);
+  if (st != SRMOE_OK) return st;
+  st = moe_ffn_gate_up(w13, s13, scale_mode, T, H, I, E1, K1, block_m, sorted_slot_ids, block_expert,
+                       num_padded, workspace, ws_bytes, stream);
+  if (st != SRMOE_OK) return st;
+  return moe_ffn_down(w2, s2, scale_mode, T, H, I, E1, K1, block_m, sorted_slot_ids, block_expert,
+                      num_padded, topk_w, workspace, ws_bytes, stream);
+}
+
+int moe_combine(int T, int K1, int H, const void* workspace, size_t ws_bytes, uint16_t* out,
+                void* stream) {
+  if (T < 0 || T > kMaxT || K1 < 1 || H <= 0) return SRMOE_ERR_INVALID_ARG;
+  if (K1 > 16 || H % 128 != 0 || (size_t)T * K1 * H >= ((size_t)1 << 31)) return SRMOE_ERR_UNSUPPORTED;
+  if (T == 0) return SRMOE_OK;
+  if (!workspace || !out || !aligned16(workspace) || !aligned16(out)) return SRMOE_ERR_INVALID_ARG;
+  if (ws_bytes < (size_t)T * K1 * H * 2) return SRMOE_ERR_WORKSPACE;
+  return hip_status(launch_combine(static_cast<const uint16_t*>(workspace), T, K1, H, out,
+                                   as_stream(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,132 @@
+// Device helpers shared by the kernels of the fused shared + routed MoE layer (gfx950).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stddef.h>
+
+namespace srmoe {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+constexpr int kGroup = 128;         // activation group / weight block edge in block-scale mode
+constexpr float kFp8Max = 448.0f;   // largest finite OCP E4M3FN magnitude
+
+// D(16x16,f32) += A(16x128,fp8 e4m3) * B(128x16,fp8 e4m3) on the gfx950 matrix cores.
+// Format code 0 selects OCP E4M3 for both operands; the E8M0 block scales are
+// fixed at 127 (= 2^0), so this is the plain unscaled product.
+// Operand layout used by every kernel here: lane l supplies row/column (l & 15)
+// and 32 consecutive K bytes starting at 32 * (l >> 4); A and B use the same
+// K mapping, so the dot products do not depend on how the hardware orders K.
+// Result: element j of lane l is D[4 * (l >> 4) + j][l & 15].
+__device__ __forceinline__ v4f mfma_16x16x128_fp8(const v8i& a, const v8i& b, const v4f& c) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
+
+// OCP FP8 E4M3FN encoding of a finite float: nearest representable value, ties
+// to the even code, saturating at +-448; the sign bit is kept (so -0 and
+// negative values that round to zero give 0x80). Written from the format
+// definition: normal range keeps 3 mantissa bits with round-to-nearest-even on
+// the float32 bit pattern and re-biases the exponent (127 -> 7); below the
+// smallest normal 2^-6 the grid is uniform with step 2^-9.
+__device__ __forceinline__ uint32_t e4m3_encode(float v) {
+  const uint32_t sign = (__float_as_uint(v) >> 24) & 0x80u;
+  const float a = fminf(fabsf(v), kFp8Max);
+  uint32_t code;
+  if (a < 0.015625f) {
+    code = (uint32_t)__float2int_rn(a * 512.0f);          // 0..8; 8 is the smallest normal
+  } else {
+    uint32_t b = __float_as_uint(a);
+    b += 0x7FFFFu + ((b >> 20) & 1u);                      // round to nearest even at mantissa bit 20
+    code = (b >> 20) - (120u << 3);                        // (exp32 << 3 | m3) - ((127 - 7) << 3)
+  }
+  return code | sign;
+}
+
+// float -> bfloat16 bits, round to nearest even (finite inputs).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+// Cross-lane moves through the DPP network (GFX9 encodings), much cheaper than the
+// LDS-routed ds_bpermute behind __shfl_xor. Lanes outside row_mask keep their value.
+enum : int {
+  kDppXor1 = 0xB1,          // quad_perm [1,0,3,2]
+  kDppXor2 = 0x4E,          // quad_perm [2,3,0,1]
+  kDppRowHalfMirror = 0x141,
+  kDppRowMirror = 0x140,
+  kDppRowBcast15 = 0x142,   // lane 15 of each row -> next row
+  kDppRowBcast31 = 0x143,   // lane 31 -> rows 2 and 3
+};
+
+template <int kCtrl, int kRowMask = 0xF>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), kCtrl,
+                                                    kRowMask, 0xF, false));
+}
+template <int kCtrl, int kRowMask = 0xF>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, kCtrl, kRowMask, 0xF, false);
+}
+
+// Max over each row of 16 lanes; every lane of the row ends with the row's max.
+__device__ __forceinline__ float row16_max(float v) {
+  v = fmaxf(v, dpp_f32<kDppXor1>(v));
+  v = fmaxf(v, dpp_f32<kDppXor2>(v));
+  v = fmaxf(v, dpp_f32<kDppRowHalfMirror>(v));
+  v = fmaxf(v, dpp_f32<kDppRowMirror>(v));
+  return v;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+  v = row16_max(v);
+  v = fmaxf(v, __shfl_xor(v, 16, kWave));
+  v = fmaxf(v, __shfl_xor(v, 32, kWave));
+  return v;
+}
+
+// Reduce max within aligned groups of `width` lanes (16, 32 or 64).
+__device__ __forceinline__ float group_max(float v, int width) {
+  v = row16_max(v);
+  if (width >= 32) v = fmaxf(v, __shfl_xor(v, 16, kWave));
+  if (width >= 64) v = fmaxf(v, __shfl_xor(v, 32, kWave));
+  return v;
+}
+
+template <int kCtrl, int kRowMask>
+__device__ __forceinline__ uint64_t max_dpp_u64(uint64_t v) {
+  const uint32_t lo = dpp_u32<kCtrl, kRowMask>((uint32_t)v);
+  const uint32_t hi = dpp_u32<kCtrl, kRowMask>((uint32_t)(v >> 32));
+  const uint64_t o = ((uint64_t)hi << 32) | lo;
+  return o > v ? o : v;
+}
+
+// Max of a 64-bit key over the wavefront, returned to every lane.
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+  v = max_dpp_u64<kDppXor1, 0xF>(v);
+  v = max_dpp_u64<kDppXor2, 0xF>(v);
+  v = max_dpp_u64<kDppRowHalfMirror, 0xF>(v);
+  v = max_dpp_u64<kDppRowMirror, 0xF>(v);
+  v = max_dpp_u64<kDppRowBcast15, 0xA>(v);
+  v = max_dpp_u64<kDppRowBcast31, 0xC>(v);   // lane 63 now holds the maximum
+  const uint32_t lo = __builtin_amdgcn_readlane((int)(uint32_t)v, 63);
+  const uint32_t hi = __builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), 63);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+// Absmax scale for FP8 quantisation, taken in float32: amax / 448, or 1 when amax == 0.
+__device__ __forceinline__ float fp8_scale(float amax) {
+  return amax > 0.0f ? __fdiv_rn(amax, kFp8Max) : 1.0f;
+}
+
+__host__ __device__ __forceinline__ size_t sorted_capacity(int T, int K1, int E1, int block_m) {
+  size_t n = (size_t)T * K1 + (size_t)E1 * (block_m - 1);
+  return (n + block_m - 1) / block_m * block_m;
+}
+
+}  // namespace srmoe

@@ -1,0 +1,126 @@
+// FP8 activation quantisation: x per token before the gate/up GEMM, and the
+// SwiGLU product `a` per sorted row before the down GEMM. Scale = amax / 448
+// (1 when amax == 0), code = E4M3FN(v / scale) with round-to-nearest-even and
+// saturation; the whole decision is taken in float32. Per-channel mode uses
+// one scale per row; block mode one per row and 128-column group. (The pages
+// run the layer in FP8 E4M3: intelliparadigm section 3.1; Optimizing GLM4-MoE
+// for production, benchmark configuration.)
+#include "common.hpp"
+
+namespace srmoe {
+
+__device__ __forceinline__ uint32_t encode4(float a, float b, float c, float d, float s) {
+  return e4m3_encode(__fdiv_rn(a, s)) | (e4m3_encode(__fdiv_rn(b, s)) << 8) |
+         (e4m3_encode(__fdiv_rn(c, s)) << 16) | (e4m3_encode(__fdiv_rn(d, s)) << 24);
+}
+
+__device__ __forceinline__ float4 load_bf16x4(const uint16_t* p) {
+  const uint2 v = *reinterpret_cast<const uint2*>(p);
+  return make_float4(bf16_to_f32(v.x & 0xFFFFu), bf16_to_f32(v.x >> 16), bf16_to_f32(v.y & 0xFFFFu),
+                     bf16_to_f32(v.y >> 16));
+}
+
+__device__ __forceinline__ float amax4(float4 v) {
+  return fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
+}
+
+// x [T,H] bf16 -> xq [T,H] e4m3, sx [T] or [T,H/128]. One 256-thread workgroup per
+// token; each thread takes 4 consecutive values per 1024-wide stripe.
+template <bool kBlock>
+__global__ void __launch_bounds__(256) quant_x_kernel(const uint16_t* __restrict__ x, int T, int H,
+                                                      uint8_t* __restrict__ xq, float* __restrict__ sx) {
+  __shared__ float red[4];
+  const int t = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const uint16_t* row = x + (size_t)t * H;
+  uint8_t* qrow = xq + (size_t)t * H;
+  if (!kBlock) {
+    float amax = 0.0f;
+    for (int h = tid * 4; h < H; h += 1024) amax = fmaxf(amax, amax4(load_bf16x4(row + h)));
+    amax = wave_max(amax);
+    if (lane == 0) red[wv] = amax;
+    __syncthreads();
+    const float scale = fp8_scale(fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3])));
+    if (tid == 0) sx[t] = scale;
+    for (int h = tid * 4; h < H; h += 1024) {
+      const float4 v = load_bf16x4(row + h);
+      *reinterpret_cast<uint32_t*>(qrow + h) = encode4(v.x, v.y, v.z, v.w, scale);
+    }
+  } else {
+    // 128-wide groups are 32 consecutive threads; H % 128 == 0 keeps every group whole.
+    for (int h0 = 0; h0 < H; h0 += 1024) {
+      const int h = h0 + tid * 4;
+      const bool in = h < H;
+      const float4 v = in ? load_bf16x4(row + h) : make_float4(0.f, 0.f, 0.f, 0.f);
+      const float scale = fp8_scale(group_max(amax4(v), 32));
+      if (in && (tid & 31) == 0) sx[(size_t)t * (H / kGroup) + h / kGroup] = scale;
+      if (in) *reinterpret_cast<uint32_t*>(qrow + h) = encode4(v.x, v.y, v.z, v.w, scale);
+    }
+  }
+}
+
+// a [P,I] float32 -> aq [P,I] e4m3, sa [P] or [P,I/128], for rows p < num_padded.
+// One 256-thread workgroup per 16 rows, 16 threads (one DPP row) per sorted row;
+// each thread takes 2 consecutive values per 32-wide stripe.
+template <bool kBlock>
+__global__ void __launch_bounds__(256) quant_a_kernel(const float* __restrict__ a, int I,
+                                                      const int32_t* __restrict__ num_padded,
+                                                      uint8_t* __restrict__ aq, float* __restrict__ sa) {
+  if (blockIdx.x * 16 >= *num_padded) return;   // num_padded is a multiple of 16
+  const int p = blockIdx.x * 16 + (threadIdx.x >> 4);
+  const int part = threadIdx.x & 15;
+  const float* row = a + (size_t)p * I;
+  uint8_t* qrow = aq + (size_t)p * I;
+  if (!kBlock) {
+    float amax = 0.0f;
+    for (int i = part * 2; i < I; i += 32) {
+      const float2 v = *reinterpret_cast<const float2*>(row + i);
+      amax = fmaxf(amax, fmaxf(fabsf(v.x), fabsf(v.y)));
+    }
+    const float scale = fp8_scale(row16_max(amax));
+    if (part == 0) sa[p] = scale;
+    for (int i = part * 2; i < I; i += 32) {
+      const float2 v = *reinterpret_cast<const float2*>(row + i);
+      *reinterpret_cast<uint16_t*>(qrow + i) =
+          (uint16_t)(e4m3_encode(__fdiv_rn(v.x, scale)) | (e4m3_encode(__fdiv_rn(v.y, scale)) << 8));
+    }
+  } else {
+    for (int g = 0; g < I; g += kGroup) {
+      float2 v[4];
+      float amax = 0.0f;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        v[j] = *reinterpret_cast<const float2*>(row + g + part * 2 + 32 * j);
+        amax = fmaxf(amax, fmaxf(fabsf(v[j].x), fabsf(v[j].y)));
+      }
+      const float scale = fp8_scale(row16_max(amax));
+      if (part == 0) sa[(size_t)p * (I / kGroup) + g / kGroup] = scale;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        *reinterpret_cast<uint16_t*>(qrow + g + part * 2 + 32 * j) =
+            (uint16_t)(e4m3_encode(__fdiv_rn(v[j].x, scale)) | (e4m3_encode(__fdiv_rn(v[j].y, scale)) << 8));
+    }
+  }
+}
+
+hipError_t launch_quant_x(const uint16_t* x, int T, int H, bool block, uint8_t* xq, float* sx,
+                          hipStream_t stream) {
+  const dim3 grid(T), blk(256);
+  if (block)
+    hipLaunchKernelGGL(quant_x_kernel<true>, grid, blk, 0, stream, x, T, H, xq, sx);
+  else
+    hipLaunchKernelGGL(quant_x_kernel<false>, grid, blk, 0, stream, x, T, H, xq, sx);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_a(const float* a, int P_max, int I, bool block, const int32_t* num_padded,
+                          uint8_t* aq, float* sa, hipStream_t stream) {
+  const dim3 grid(P_max / 16), blk(256);
+  if (block)
+    hipLaunchKernelGGL(quant_a_kernel<true>, grid, blk, 0, stream, a, I, num_padded, aq, sa);
+  else
+    hipLaunchKernelGGL(quant_a_kernel<false>, grid, blk, 0, stream, a, I, num_padded, aq, sa);
+  return hipGetLastError();
+}
+
+}  // namespace srmoe

@@ -1,0 +1,106 @@
+"""Buffers and call sequence for one fused shared + routed MoE layer on the GPU.
+
+Torch provides device memory and the stream; every step of the layer runs in
+libsrmoe.so's HIP kernels through the four C calls (route, align, fused FFN,
+combine).
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import numpy as np
+import torch
+
+from . import _lib as L
+
+
+@dataclass
+class DeviceWeights:
+    w13: torch.Tensor   # uint8 [E1, 2I, H]
+    s13: torch.Tensor   # float32
+    w2: torch.Tensor    # uint8 [E1, H, I]
+    s2: torch.Tensor    # float32
+    scale_mode: int
+
+    @staticmethod
+    def from_numpy(w13_q, s13, w2_q, s2, device="cuda"):
+        mode = L.SCALE_PER_CHANNEL if s13.ndim == 2 else L.SCALE_BLOCK128
+        up = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(device)
+        return DeviceWeights(up(w13_q), up(s13), up(w2_q), up(s2), mode)
+
+
+class FusedMoE:
+    """One layer's routing tables, sort arrays, workspaces and output for fixed sizes."""
+
+    def __init__(self, T, H, I, E, K, block_m, scale_mode, device="cuda"):
+        self.T, self.H, self.I, self.E, self.K = T, H, I, E, K
+        self.E1, self.K1 = E + 1, K + 1
+        self.block_m, self.scale_mode = block_m, scale_mode
+        dev = torch.device(device)
+        i32 = dict(dtype=torch.int32, device=dev)
+        self.P_max = L.moe_sorted_capacity(T, self.K1, self.E1, block_m)
+        self.topk_ids = torch.empty((T, self.K1), **i32)
+        self.topk_w = torch.empty((T, self.K1), dtype=torch.float32, device=dev)
+        self.sorted_slot_ids = torch.empty(self.P_max, **i32)
+        self.block_expert = torch.empty(self.P_max // block_m, **i32)
+        self.expert_counts = torch.empty(self.E1, **i32)
+        self.expert_offsets = torch.empty(self.E1 + 1, **i32)
+        self.num_padded = torch.empty(1, **i32)
+        self.align_ws_bytes = L.moe_align_workspace_bytes(T, self.K1, self.E1)
+        self.align_ws = torch.empty(self.align_ws_bytes, dtype=torch.uint8, device=dev)
+        self.ws_bytes = L.moe_ffn_workspace_bytes(T, H, I, self.E1, self.K1, block_m, scale_mode)
+        if self.ws_bytes == 0:
+            raise ValueError("unsupported FFN shape")
+        self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device=dev)
+        self.out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+        self.offsets = L.moe_ffn_workspace_offsets(T, H, I, self.E1, self.K1, block_m, scale_mode)
+
+    def dims(self):
+        return (self.T, self.H, self.I, self.E1, self.K1, self.block_m)
+
+    def route(self, logits, shared_weight=1.0, stream=None):
+        L.moe_route_topk_plus_shared(logits, self.T, self.E, self.K, shared_weight, self.topk_ids,
+                                     self.topk_w, stream)
+
+    def align(self, stream=None):
+        L.moe_align_by_expert(self.topk_ids, self.T, self.K1, self.E1, self.block_m,
+                              self.sorted_slot_ids, self.block_expert, self.expert_counts,
+                              self.expert_offsets, self.num_padded, self.align_ws,
+                              self.align_ws_bytes, stream)
+
+    def ffn(self, x, W: DeviceWeights, stream=None):
+        T, H, I, E1, K1, bm = self.dims()
+        L.moe_fused_ffn(x, W.w13, W.s13, W.w2, W.s2, self.scale_mode, T, H, I, E1, K1, bm,
+                        self.sorted_slot_ids, self.block_expert, self.num_padded, self.topk_w,
+                        self.ws, self.ws_bytes, stream)
+
+    def ffn_stages(self, x, W: DeviceWeights, stream=None, between=None):
+        """The FFN as its three C stages; `between(name)` is called after each launch."""
+        T, H, I, E1, K1, bm = self.dims()
+        L.moe_ffn_quant_x(x, self.scale_mode, T, H, I, E1, K1, bm, self.ws, self.ws_bytes, stream)
+        if between:
+            between("quant_x")
+        L.moe_ffn_gate_up(W.w13, W.s13, self.scale_mode, T, H, I, E1, K1, bm, self.sorted_slot_ids,
+                          self.block_expert, self.num_padded, self.ws, self.ws_bytes, stream)
+        if between:
+            between("gate_up")
+        L.moe_ffn_down(W.w2, W.s2, self.scale_mode, T, H, I, E1, K1, bm, self.sorted_slot_ids,
+                       self.block_expert, self.num_padded, self.topk_w, self.ws, self.ws_bytes, stream)
+        if between:
+            between("down")
+
+    def combine(self, stream=None):
+        L.moe_combine(self.T, self.K1, self.H, self.ws, self.ws_bytes, self.out, stream)
+
+    def forward(self, x, logits, W: DeviceWeights, shared_weight=1.0, stream=None):
+        self.route(logits, shared_weight, stream)
+        self.align(stream)
+        self.ffn(x, W, stream)
+        self.combine(stream)
+        return self.out
+
+    # views into the workspace, for inspecting the stages
+    def ws_view(self, name, dtype, shape):
+        off = self.offsets[name]
+        n = int(np.prod(shape)) * torch.empty((), dtype=dtype).element_size()
+        return self.ws[off:off + n].view(dtype).view(*shape)

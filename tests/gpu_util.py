@@ -1,0 +1,150 @@
+"""Helpers of the GPU parity tests: upload seeded inputs, run the C calls, fetch results."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+from workloads import MoEConfig, generate, f32_from_bf16_bits
+
+DEV = "cuda:0"
+TOL = 2e-2   # max per-token relative error (inf-norm) of the bf16 layer output
+
+
+def note(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def to_dev(a, dtype=None):
+    t = torch.from_numpy(np.ascontiguousarray(a))
+    if dtype is not None:
+        t = t.view(dtype)
+    return t.to(DEV)
+
+
+def bf16_dev(bits: np.ndarray):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(DEV).view(torch.bfloat16)
+
+
+def bf16_to_np(t: torch.Tensor) -> np.ndarray:
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+def token_rel_err(got: np.ndarray, ref: np.ndarray) -> np.ndarray:
+    """Per-row inf-norm relative error max|g - r| / max|r|."""
+    den = np.max(np.abs(ref), axis=1)
+    return np.max(np.abs(got - ref), axis=1) / np.where(den > 0, den, 1.0)
+
+
+def make_layer(inp, block_m):
+    from shared_routed_expert_amd import FusedMoE, DeviceWeights
+    c = inp.cfg
+    W = DeviceWeights.from_numpy(inp.w13_q, inp.s13, inp.w2_q, inp.s2, device=DEV)
+    layer = FusedMoE(c.T, c.H, c.I, c.E, c.K, block_m, W.scale_mode, device=DEV)
+    return layer, W
+
+
+def run_layer(inp, block_m, shared_weight=1.0, layer=None, W=None):
+    if layer is None:
+        layer, W = make_layer(inp, block_m)
+    x = bf16_dev(inp.x_bf16)
+    lg = to_dev(inp.logits)
+    layer.forward(x, lg, W, shared_weight)
+    torch.cuda.synchronize()
+    return layer, W
+
+
+def small_cfg(name, T, H, I, E, K, mode="channel", seed=0, zipf=None):
+    return MoEConfig(name, T=T, H=H, E=E, K=K, I=I, scale_mode=mode, seed=seed, zipf_s=zipf)
+
+
+def x_f32(inp):
+    return f32_from_bf16_bits(inp.x_bf16)
+
+
+__all__ = ["DEV", "TOL", "note", "to_dev", "bf16_dev", "bf16_to_np", "token_rel_err", "make_layer",
+           "run_layer", "small_cfg", "x_f32", "generate"]
+
+
+# ---------------------------------------------------------------------------- FP8 tie allowance
+# The FP8 code of each element of the SwiGLU product a is decided in float32 on both sides,
+# but a itself comes out of a float32 GEMM on the GPU and a float64 GEMM in the oracle. An
+# element whose value lies within the accumulation-error bound of a rounding tie may land on
+# either side, and both codes are correct roundings of the same definition. A row that misses
+# the plain 2e-2 bar is re-checked with an allowance equal to the effect of moving exactly those
+# near-tie codes by one step.
+import oracle as _oracle
+from oracle import moe as _om
+
+EPS32 = 2.0 ** -24
+
+
+def _a_row_and_window(inp, t, e):
+    c = inp.cfg
+    group = None if inp.s13.ndim == 2 else 128
+    xq, sx = _oracle.quantize_act(x_f32(inp)[t:t + 1], group)
+    xd = _om.dequant_act(xq, sx, group)[0]
+    w13 = _oracle.dequant_weight(inp.w13_q[e], inp.s13[e])
+    wg, wu = w13[:c.I], w13[c.I:]
+    g, u = wg @ xd, wu @ xd
+    G1, U1 = np.abs(wg) @ np.abs(xd), np.abs(wu) @ np.abs(xd)
+    # float32 accumulation bound over H products (128 per matrix-core step), with 4x margin
+    gamma = 4.0 * (16 + c.H / 128) * EPS32
+    sig = 1.0 / (1.0 + np.exp(-g))
+    silu = g * sig
+    dsilu = sig * (1.0 + g * (1.0 - sig))
+    a = silu * u
+    win = gamma * (np.abs(dsilu * u) * G1 + np.abs(silu) * U1) + 16 * EPS32 * np.abs(a)
+    return a, win
+
+
+def _e4m3_step(v):
+    av = np.abs(v)
+    e = np.floor(np.log2(np.maximum(av, 2.0 ** -6)))
+    return np.where(av < 2.0 ** -6, 2.0 ** -9, 2.0 ** (e - 3))
+
+
+def slot_allowance(inp, t, e):
+    """Per-column bound [H] on how far y = W2 a' may move when the near-tie codes of a' flip."""
+    c = inp.cfg
+    a, win = _a_row_and_window(inp, t, e)
+    gsz = c.I if inp.s13.ndim == 2 else 128
+    w2 = np.abs(_oracle.dequant_weight(inp.w2_q[e], inp.s2[e]))
+    allow = np.zeros(c.H)
+    for g0 in range(0, c.I, gsz):
+        sl = slice(g0, g0 + gsz)
+        ag, wg_ = a[sl], win[sl]
+        amax = np.abs(ag).max()
+        if amax == 0:
+            continue
+        s = float(np.float32(np.float32(amax) / np.float32(448.0)))
+        v = ag / s
+        step = _e4m3_step(v)
+        base = np.where(np.abs(v) < 2.0 ** -6, 0.0, 2.0 ** np.floor(np.log2(np.maximum(np.abs(v), 2.0 ** -6))))
+        frac = (np.abs(v) - base) / step
+        dist = np.abs(frac - np.floor(frac) - 0.5) * step
+        # the scale itself follows amax, which carries its own window
+        near = dist <= (wg_ / s + np.abs(v) * (wg_[np.argmax(np.abs(ag))] / amax)) * 1.0 + 1e-12
+        if near.any():
+            idx = np.nonzero(near)[0]
+            allow += w2[:, g0 + idx] @ (step[idx] * s)
+    return allow
+
+
+def check_rows_with_ties(got, ref, inp, rows, ids, w, tol=TOL):
+    """got/ref [n,H]; rows[j] lists the (token, slot) pairs summed into row j (with weights w).
+    Passes rows within tol (per-row inf-norm relative); re-checks the others with the tie
+    allowance. Returns (max plain error, number of rows that needed the allowance)."""
+    err = token_rel_err(got, ref)
+    bad = np.nonzero(err > tol)[0]
+    for j in bad:
+        allow = np.zeros(ref.shape[1])
+        for (t, k) in rows[j]:
+            allow += abs(float(w[t, k])) * slot_allowance(inp, t, int(ids[t, k]))
+        den = np.abs(ref[j]).max()
+        ok = np.abs(got[j] - ref[j]) <= tol * den + allow * 1.0001 + 1e-30
+        assert ok.all(), (f"row {j}: rel err {err[j]:.4f} exceeds {tol} even with the FP8 tie allowance "
+                          f"(max excess {np.max(np.abs(got[j] - ref[j]) - tol * den - allow):.3e})")
+    return float(err.max()), len(bad)

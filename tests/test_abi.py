@@ -1,0 +1,175 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports every
+function include/srmoe.h declares, and rejects bad arguments before any launch.
+
+Only invalid calls are made here: each returns from the host-side checks, so no
+HIP call is issued (the pointers are fake, 16-byte aligned integers).
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "srmoe.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    from shared_routed_expert_amd import build as b
+    if not os.path.exists(b.LIB):
+        b.build()
+    from shared_routed_expert_amd import _lib
+    return _lib
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*([a-z_][a-z0-9_]*)\s*\(",
+                                 src, flags=re.M)))
+
+
+def test_header_declares_the_four_calls():
+    names = declared_functions()
+    for n in ("moe_route_topk_plus_shared", "moe_align_by_expert", "moe_fused_ffn", "moe_combine"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(L):
+    names = declared_functions()
+    assert len(names) >= 12
+    out = subprocess.run(["nm", "-D", "--defined-only", L.LIB_PATH], capture_output=True, text=True).stdout
+    exported = {l.split()[-1] for l in out.splitlines() if " T " in l}
+    missing = [n for n in names if n not in exported]
+    assert not missing, missing
+    for n in names:
+        getattr(L.lib, n)  # resolvable through ctypes
+    assert set(L.EXPORTED) == set(names)
+
+
+def test_status_strings(L):
+    for st in (0, -1, -2, -3, -4):
+        assert L.lib.srmoe_status_string(st)
+    assert L.lib.srmoe_last_hip_error() == 0
+
+
+def test_capacity_and_workspace_sizes(L):
+    from oracle import sorted_capacity
+    for T, K1, E1, bm in [(64, 9, 161, 16), (4096, 9, 161, 64), (16384, 9, 161, 128), (0, 3, 9, 16), (16, 3, 9, 32)]:
+        assert L.moe_sorted_capacity(T, K1, E1, bm) == sorted_capacity(T, K1, E1, bm)
+    assert L.moe_sorted_capacity(16, 3, 9, 48) == 0
+    off = L.moe_ffn_workspace_offsets(64, 5120, 192, 161, 9, 16, 0)
+    assert off["slot_out"] == 0
+    assert off["total"] == L.moe_ffn_workspace_bytes(64, 5120, 192, 161, 9, 16, 0)
+    keys = ["slot_out", "xq", "sx", "a", "aq", "sa", "total"]
+    vals = [off[k] for k in keys]
+    assert vals == sorted(vals) and all(v % 256 == 0 for v in vals)
+    assert off["xq"] >= 64 * 9 * 5120 * 2
+    assert L.moe_ffn_workspace_bytes(64, 5000, 192, 161, 9, 16, 0) == 0     # H % 128
+    assert L.moe_ffn_workspace_bytes(64, 5120, 192, 161, 9, 16, 1) == 0     # block mode, I % 128
+    assert L.moe_ffn_workspace_bytes(64, 5120, 1536, 161, 9, 16, 1) > 0
+    assert L.moe_align_workspace_bytes(16384, 9, 161) >= 144 * 161 * 4
+
+
+FAKE = 0x10000          # aligned fake device pointers: never dereferenced on these paths
+MIS = 0x10004           # misaligned
+
+
+def test_route_rejects(L):
+    f = lambda *a: L.moe_route_topk_plus_shared(*a, stream=0, check=False)
+    assert f(FAKE, -1, 160, 8, 1.0, FAKE, FAKE) == -1
+    assert f(FAKE, 4, 0, 0, 1.0, FAKE, FAKE) == -1
+    assert f(FAKE, 4, 160, -1, 1.0, FAKE, FAKE) == -1
+    assert f(FAKE, 4, 256, 8, 1.0, FAKE, FAKE) == -2
+    assert f(FAKE, 4, 8, 9, 1.0, FAKE, FAKE) == -2
+    assert f(FAKE, 4, 160, 16, 1.0, FAKE, FAKE) == -2
+    assert f(None, 4, 160, 8, 1.0, FAKE, FAKE) == -1
+    assert f(FAKE, 4, 160, 8, 1.0, None, FAKE) == -1
+    assert f(MIS, 4, 160, 8, 1.0, FAKE, FAKE) == -1
+    assert f(FAKE, 0, 160, 8, 1.0, None, None) == 0     # T == 0: nothing to do, nothing launched
+
+
+def test_align_rejects(L):
+    def f(T=64, K1=9, E1=161, bm=16, ptrs=None, ws=FAKE, ws_bytes=1 << 20):
+        p = ptrs or [FAKE] * 6
+        return L.moe_align_by_expert(p[0], T, K1, E1, bm, p[1], p[2], p[3], p[4], p[5], ws, ws_bytes,
+                                     stream=0, check=False)
+    assert f(T=-1) == -1
+    assert f(K1=0) == -1
+    assert f(K1=17) == -2
+    assert f(E1=257) == -2
+    for bm in (0, 8, 48, 256):
+        assert f(bm=bm) == -2
+    for i in range(6):
+        p = [FAKE] * 6
+        p[i] = None
+        assert f(ptrs=p) == -1
+        p[i] = MIS
+        assert f(ptrs=p) == -1
+    assert f(ws=None) == -1
+    assert f(T=16384, ws_bytes=1024) == -3
+
+
+def _ffn_args(**kw):
+    a = dict(x=FAKE, w13=FAKE, s13=FAKE, w2=FAKE, s2=FAKE, scale_mode=0, T=64, H=5120, I=192, E1=161,
+             K1=9, block_m=16, sorted_slot_ids=FAKE, block_expert=FAKE, num_padded=FAKE, topk_w=FAKE,
+             workspace=FAKE, ws_bytes=1 << 40)
+    a.update(kw)
+    return a
+
+
+def test_ffn_rejects(L):
+    f = lambda **kw: L.moe_fused_ffn(**_ffn_args(**kw), stream=0, check=False)
+    assert f(T=-1) == -1
+    assert f(H=0) == -1
+    assert f(I=-32) == -1
+    assert f(scale_mode=2) == -1
+    assert f(H=5000) == -2
+    assert f(I=200) == -2
+    assert f(scale_mode=1, I=192) == -2
+    assert f(E1=300) == -2
+    assert f(K1=17) == -2
+    assert f(block_m=24) == -2
+    assert f(T=1 << 21) == -1
+    for name in ("x", "w13", "s13", "w2", "s2", "sorted_slot_ids", "block_expert", "num_padded",
+                 "topk_w", "workspace"):
+        assert f(**{name: None}) == -1, name
+        assert f(**{name: MIS}) == -1, name
+    need = L.moe_ffn_workspace_bytes(64, 5120, 192, 161, 9, 16, 0)
+    assert f(ws_bytes=need - 1) == -3
+    assert f(T=0, x=None) == 0
+
+
+def test_ffn_stage_rejects(L):
+    a = _ffn_args()
+    assert L.moe_ffn_quant_x(FAKE, 0, 64, 5120, 192, 161, 9, 16, None, 1 << 40, stream=0, check=False) == -1
+    assert L.moe_ffn_quant_x(FAKE, 0, 64, 5120, 192, 161, 9, 16, FAKE, 10, stream=0, check=False) == -3
+    assert L.moe_ffn_gate_up(FAKE, None, 0, 64, 5120, 192, 161, 9, 16, FAKE, FAKE, FAKE, FAKE, 1 << 40,
+                             stream=0, check=False) == -1
+    assert L.moe_ffn_down(FAKE, FAKE, 0, 64, 5120, 192, 161, 9, 16, FAKE, FAKE, FAKE, None, FAKE, 1 << 40,
+                          stream=0, check=False) == -1
+    assert L.moe_ffn_down(FAKE, FAKE, 0, 64, 5120, 192, 161, 9, 64, FAKE, FAKE, FAKE, FAKE, FAKE, 100,
+                          stream=0, check=False) == -3
+    del a
+
+
+def test_combine_rejects(L):
+    f = lambda *a: L.moe_combine(*a, stream=0, check=False)
+    assert f(-1, 9, 5120, FAKE, 1 << 30, FAKE) == -1
+    assert f(64, 0, 5120, FAKE, 1 << 30, FAKE) == -1
+    assert f(64, 9, 5000, FAKE, 1 << 30, FAKE) == -2
+    assert f(64, 9, 5120, None, 1 << 30, FAKE) == -1
+    assert f(64, 9, 5120, FAKE, 1 << 30, MIS) == -1
+    assert f(64, 9, 5120, FAKE, 64 * 9 * 5120 * 2 - 1, FAKE) == -3
+    assert f(0, 9, 5120, None, 0, None) == 0
+
+
+def test_no_cpu_fallback_in_product(L):
+    """The product path never imports the oracle."""
+    pkg = os.path.join(ROOT, "shared_routed_expert_amd")
+    for fn in os.listdir(pkg):
+        if fn.endswith(".py"):
+            src = open(os.path.join(pkg, fn)).read()
+            assert "import oracle" not in src and "from oracle" not in src, fn
