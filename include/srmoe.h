@@ -117,8 +117,8 @@ int moe_align_by_expert(const int32_t* topk_ids, int T, int K1, int E1, int bloc
  *   sorted_slot_ids, block_expert, num_padded: outputs of step 2 (same block_m)
  *   topk_w   [T,K1] float32 routing weights (step 1)
  *   workspace >= moe_ffn_workspace_bytes(...) bytes; also read by moe_combine
- *   limits: H % 128 == 0; I % 32 == 0 (block mode: I % 128 == 0); E1 <= 256;
- *           1 <= K1 <= 16; block_m in {16,32,64,128}.
+ *   limits: H % 128 == 0, H <= 65536; I % 32 == 0 (block mode: I % 128 == 0),
+ *           I <= 3072; E1 <= 256; 1 <= K1 <= 16; block_m in {16,32,64,128}.
  * ------------------------------------------------------------------------- */
 int moe_fused_ffn(const uint16_t* x, const uint8_t* w13, const float* s13, const uint8_t* w2,
                   const float* s2, int scale_mode, int T, int H, int I, int E1, int K1,
@@ -155,10 +155,11 @@ size_t moe_align_workspace_bytes(int T, int K1, int E1);
 size_t moe_ffn_workspace_bytes(int T, int H, int I, int E1, int K1, int block_m, int scale_mode);
 /* Byte offsets inside the FFN workspace (host): out[0] slot_out [T*K1,H] bf16 (always 0),
  * out[1] x_q [T,H] e4m3, out[2] x scales, out[3] a [P_max,I] float32 (sorted-row order),
- * out[4] a_q [P_max,I] e4m3, out[5] a scales, out[6] total. For inspecting the stages;
- * returns SRMOE_OK or SRMOE_ERR_INVALID_ARG / SRMOE_ERR_UNSUPPORTED for bad shapes. */
+ * out[4] a_q [P_max,I] e4m3, out[5] a scales, out[6] per-row output scales [P_max] float32,
+ * out[7] total. For inspecting the stages; returns SRMOE_OK or SRMOE_ERR_INVALID_ARG /
+ * SRMOE_ERR_UNSUPPORTED for bad shapes. */
 int moe_ffn_workspace_offsets(int T, int H, int I, int E1, int K1, int block_m, int scale_mode,
-                              size_t* out /* host, 7 entries */);
+                              size_t* out /* host, 8 entries */);
 const char* srmoe_status_string(int status);
 int srmoe_last_hip_error(void); /* hipError_t of this thread's last failed launch, 0 if none */
 

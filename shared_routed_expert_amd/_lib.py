@@ -99,11 +99,11 @@ def moe_ffn_workspace_bytes(T, H, I, E1, K1, block_m, scale_mode):
 
 
 def moe_ffn_workspace_offsets(T, H, I, E1, K1, block_m, scale_mode):
-    """Returns a dict of byte offsets: slot_out, xq, sx, a, aq, sa, total."""
-    arr = (ctypes.c_size_t * 7)()
+    """Returns a dict of byte offsets: slot_out, xq, sx, a, aq, sa, rs, total."""
+    arr = (ctypes.c_size_t * 8)()
     _check("moe_ffn_workspace_offsets",
            lib.moe_ffn_workspace_offsets(T, H, I, E1, K1, block_m, scale_mode, arr))
-    return dict(zip(("slot_out", "xq", "sx", "a", "aq", "sa", "total"), list(arr)))
+    return dict(zip(("slot_out", "xq", "sx", "a", "aq", "sa", "rs", "total"), list(arr)))
 
 
 def moe_route_topk_plus_shared(logits, T, E, K, shared_weight, topk_ids, topk_w, stream=None, check=True):

@@ -10,8 +10,8 @@
 // sentinel T*K1. Nothing depends on atomics or scheduling, so the output is
 // the unique stable order.
 //
-// Small inputs (<= 4 chunks) run as one workgroup; larger ones as count ->
-// scan -> scatter.
+// Small inputs (<= 4 chunks) run as one workgroup whose 4 wavefronts take
+// consecutive quarters of the entries; larger ones as count -> scan -> scatter.
 #include "common.hpp"
 
 namespace srmoe {
@@ -32,26 +32,25 @@ __device__ __forceinline__ uint64_t lanes_with_same_expert(int e, bool valid) {
 
 constexpr int kPerLane = kChunk / kWave;   // 16 entries of a chunk per lane
 
-// Load one chunk's expert ids into registers: entry start + 64*i + lane -> ev[i] (-1 past N).
+// A wavefront's chunk is the entry range [start, end), at most kChunk long.
+// Load its expert ids into registers: entry start + 64*i + lane -> ev[i] (-1 past end).
 // All loads are issued together, so a chunk costs one memory round trip.
-__device__ __forceinline__ void load_chunk(const int32_t* __restrict__ ids, int N, int chunk,
+__device__ __forceinline__ void load_chunk(const int32_t* __restrict__ ids, int start, int end,
                                            int (&ev)[kPerLane]) {
   const int lane = threadIdx.x & 63;
-  const int start = chunk * kChunk;
 #pragma unroll
   for (int i = 0; i < kPerLane; ++i) {
     const int s = start + i * kWave + lane;
-    ev[i] = s < N ? ids[s] : -1;
+    ev[i] = s < end ? ids[s] : -1;
   }
 }
 
 // Count the entries of one chunk into cnt[0..E1) (LDS, zeroed by the caller).
-__device__ __forceinline__ void count_chunk(const int (&ev)[kPerLane], int N, int chunk, int* cnt) {
+__device__ __forceinline__ void count_chunk(const int (&ev)[kPerLane], int start, int end, int* cnt) {
   const int lane = threadIdx.x & 63;
-  const int start = chunk * kChunk;
 #pragma unroll
   for (int i = 0; i < kPerLane; ++i) {
-    if (start + i * kWave >= N) break;
+    if (start + i * kWave >= end) break;
     const bool valid = ev[i] >= 0;
     const int e = valid ? ev[i] : 0;
     const uint64_t m = lanes_with_same_expert(e, valid);
@@ -61,14 +60,13 @@ __device__ __forceinline__ void count_chunk(const int (&ev)[kPerLane], int N, in
 }
 
 // Scatter one chunk: run[e] (LDS) starts at the chunk's first output position for e.
-__device__ __forceinline__ void scatter_chunk(const int (&ev)[kPerLane], int N, int chunk, int* run,
+__device__ __forceinline__ void scatter_chunk(const int (&ev)[kPerLane], int start, int end, int* run,
                                               int32_t* __restrict__ sorted) {
   const int lane = threadIdx.x & 63;
   const uint64_t lower = (1ull << lane) - 1ull;
-  const int start = chunk * kChunk;
 #pragma unroll
   for (int i = 0; i < kPerLane; ++i) {
-    if (start + i * kWave >= N) break;
+    if (start + i * kWave >= end) break;
     const int s = start + i * kWave + lane;
     const bool valid = ev[i] >= 0;
     const int e = valid ? ev[i] : 0;
@@ -135,12 +133,14 @@ __global__ void __launch_bounds__(256) align_small_kernel(
   __shared__ int off[kMaxE1];
   __shared__ int lds4[4];
   const int wv = threadIdx.x >> 6;
-  const int nchunks = (N + kChunk - 1) / kChunk;
+  // the N <= 4*kChunk entries are split over the 4 wavefronts in order, in whole 64s
+  const int per = ((N + 4 * kWave - 1) / (4 * kWave)) * kWave;
+  const int start = min(wv * per, N), end = min(start + per, N);
   int ev[kPerLane];
-  load_chunk(ids, N, wv, ev);
+  load_chunk(ids, start, end, ev);
   for (int i = threadIdx.x; i < 4 * kMaxE1; i += blockDim.x) (&cnt[0][0])[i] = 0;
   __syncthreads();
-  if (wv < nchunks) count_chunk(ev, N, wv, cnt[wv]);
+  count_chunk(ev, start, end, cnt[wv]);
   __syncthreads();
   const int e = threadIdx.x;
   int total_e = 0;
@@ -157,7 +157,7 @@ __global__ void __launch_bounds__(256) align_small_kernel(
     }
   }
   __syncthreads();
-  if (wv < nchunks) scatter_chunk(ev, N, wv, cnt[wv], sorted);
+  scatter_chunk(ev, start, end, cnt[wv], sorted);
 }
 
 // Large inputs. Pass 1: per-chunk counts -> chunk_counts[chunk][E1].
@@ -170,9 +170,10 @@ __global__ void __launch_bounds__(256) align_count_kernel(const int32_t* __restr
   for (int i = lane; i < kMaxE1; i += kWave) cnt[wv][i] = 0;
   __builtin_amdgcn_wave_barrier();
   if (chunk >= nchunks) return;
+  const int start = chunk * kChunk, end = min(start + kChunk, N);
   int ev[kPerLane];
-  load_chunk(ids, N, chunk, ev);
-  count_chunk(ev, N, chunk, cnt[wv]);
+  load_chunk(ids, start, end, ev);
+  count_chunk(ev, start, end, cnt[wv]);
   __builtin_amdgcn_wave_barrier();
   for (int i = lane; i < E1; i += kWave) chunk_counts[(size_t)chunk * E1 + i] = cnt[wv][i];
 }
@@ -213,11 +214,12 @@ __global__ void __launch_bounds__(256) align_scatter_kernel(const int32_t* __res
   const int chunk = blockIdx.x * 4 + wv;
   const int nchunks = (N + kChunk - 1) / kChunk;
   if (chunk >= nchunks) return;
+  const int start = chunk * kChunk, end = min(start + kChunk, N);
   int ev[kPerLane];
-  load_chunk(ids, N, chunk, ev);
+  load_chunk(ids, start, end, ev);
   for (int i = lane; i < E1; i += kWave) run[wv][i] = chunk_base[(size_t)chunk * E1 + i];
   __builtin_amdgcn_wave_barrier();
-  scatter_chunk(ev, N, chunk, run[wv], sorted);
+  scatter_chunk(ev, start, end, run[wv], sorted);
 }
 
 size_t align_workspace_bytes(int T, int K1, int E1) {

@@ -10,14 +10,18 @@ size_t align_workspace_bytes(int T, int K1, int E1);
 hipError_t launch_align(const int32_t*, int, int, int, int, int32_t*, int32_t*, int32_t*, int32_t*,
                         int32_t*, void*, hipStream_t);
 hipError_t launch_quant_x(const uint16_t*, int, int, bool, uint8_t*, float*, hipStream_t);
-hipError_t launch_quant_a(const float*, int, int, bool, const int32_t*, uint8_t*, float*, hipStream_t);
+hipError_t launch_quant_a(const float*, int, int, bool, const int32_t*, const float*, int, uint8_t*,
+                          float*, float*, hipStream_t);
 hipError_t launch_gate_up(const uint8_t*, const float*, const uint8_t*, const float*, bool,
-                          const int32_t*, const int32_t*, const int32_t*, float*, int, int, int, int,
-                          int, int, hipStream_t);
+                          const int32_t*, const int32_t*, float*, int, int, int, int, int, int,
+                          hipStream_t);
 hipError_t launch_down(const uint8_t*, const float*, const uint8_t*, const float*, bool,
-                       const int32_t*, const int32_t*, const int32_t*, const float*, uint16_t*, int,
-                       int, int, int, int, int, hipStream_t);
+                       const int32_t*, const int32_t*, const float*, uint16_t*, int, int, int, int,
+                       int, int, hipStream_t);
 hipError_t launch_combine(const uint16_t*, int, int, int, uint16_t*, hipStream_t);
+hipError_t launch_gate_up_decode(const uint8_t*, const float*, const uint8_t*, const float*, bool,
+                                 const int32_t*, const int32_t*, float*, int, int, int, int, int,
+                                 hipStream_t);
 }  // namespace srmoe
 
 using namespace srmoe;
@@ -39,9 +43,10 @@ int hip_status(hipError_t e) {
 }
 
 // FFN workspace: slot_out first (moe_combine reads it at offset 0), then the
-// quantised activations, the SwiGLU product in float32 and its quantised copy.
+// quantised activations, the SwiGLU product in float32, its quantised copy and
+// the per-row output scale of the down GEMM.
 struct FfnLayout {
-  size_t slot_out, xq, sx, a, aq, sa, total;
+  size_t slot_out, xq, sx, a, aq, sa, rs, total;
 };
 
 FfnLayout ffn_layout(int T, int H, int I, int E1, int K1, int block_m, int mode) {
@@ -56,6 +61,7 @@ FfnLayout ffn_layout(int T, int H, int I, int E1, int K1, int block_m, int mode)
   L.a = off;        off += al256(P * I * 4);
   L.aq = off;       off += al256(P * I);
   L.sa = off;       off += al256(P * gi * 4);
+  L.rs = off;       off += al256(P * 4);
   L.total = off;
   return L;
 }
@@ -71,7 +77,7 @@ int check_ffn_dims(int scale_mode, int T, int H, int I, int E1, int K1, int bloc
   if (!valid_block_m(block_m)) return SRMOE_ERR_UNSUPPORTED;
   if (H % 128 != 0 || I % 32 != 0) return SRMOE_ERR_UNSUPPORTED;
   if (scale_mode == SRMOE_SCALE_BLOCK128 && I % 128 != 0) return SRMOE_ERR_UNSUPPORTED;
-  if (H > 65536 || I > 16384) return SRMOE_ERR_UNSUPPORTED;
+  if (H > 65536 || I > 3072) return SRMOE_ERR_UNSUPPORTED;
   if ((size_t)T * K1 * H >= ((size_t)1 << 31)) return SRMOE_ERR_UNSUPPORTED;
   return SRMOE_OK;
 }
@@ -103,7 +109,7 @@ int moe_ffn_workspace_offsets(int T, int H, int I, int E1, int K1, int block_m, 
   if (!out) return SRMOE_ERR_INVALID_ARG;
   const FfnLayout L = ffn_layout(T, H, I, E1, K1, block_m, scale_mode);
   out[0] = L.slot_out; out[1] = L.xq; out[2] = L.sx; out[3] = L.a; out[4] = L.aq; out[5] = L.sa;
-  out[6] = L.total;
+  out[6] = L.rs; out[7] = L.total;
   return SRMOE_OK;
 }
 
@@ -180,9 +186,15 @@ int moe_ffn_gate_up(const uint8_t* w13, const float* s13, int scale_mode, int T,
   if (ws_bytes < L.total) return SRMOE_ERR_WORKSPACE;
   char* ws = static_cast<char*>(workspace);
   const bool blk = scale_mode == SRMOE_SCALE_BLOCK128;
+  if (block_m == 16)
+    return hip_status(launch_gate_up_decode(reinterpret_cast<const uint8_t*>(ws + L.xq),
+                                            reinterpret_cast<const float*>(ws + L.sx), w13, s13, blk,
+                                            sorted_slot_ids, block_expert,
+                                            reinterpret_cast<float*>(ws + L.a), T, H, I, E1, K1,
+                                            as_stream(stream)));
   return hip_status(launch_gate_up(reinterpret_cast<const uint8_t*>(ws + L.xq),
                                    reinterpret_cast<const float*>(ws + L.sx), w13, s13, blk,
-                                   sorted_slot_ids, block_expert, num_padded,
+                                   sorted_slot_ids, block_expert,
                                    reinterpret_cast<float*>(ws + L.a), T, H, I, E1, K1, block_m,
                                    as_stream(stream)));
 }
@@ -204,13 +216,15 @@ int moe_ffn_down(const uint8_t* w2, const float* s2, int scale_mode, int T, int 
   char* ws = static_cast<char*>(workspace);
   const bool blk = scale_mode == SRMOE_SCALE_BLOCK128;
   const int P_max = (int)sorted_capacity(T, K1, E1, block_m);
-  hipError_t e = launch_quant_a(reinterpret_cast<const float*>(ws + L.a), P_max, I, blk, num_padded,
+  hipError_t e = launch_quant_a(reinterpret_cast<const float*>(ws + L.a), P_max, I, blk,
+                                sorted_slot_ids, topk_w, T * K1,
                                 reinterpret_cast<uint8_t*>(ws + L.aq),
-                                reinterpret_cast<float*>(ws + L.sa), as_stream(stream));
+                                reinterpret_cast<float*>(ws + L.sa),
+                                reinterpret_cast<float*>(ws + L.rs), as_stream(stream));
   if (e != hipSuccess) return hip_status(e);
   return hip_status(launch_down(reinterpret_cast<const uint8_t*>(ws + L.aq),
                                 reinterpret_cast<const float*>(ws + L.sa), w2, s2, blk,
-                                sorted_slot_ids, block_expert, num_padded, topk_w,
+                                sorted_slot_ids, block_expert, reinterpret_cast<const float*>(ws + L.rs),
                                 reinterpret_cast<uint16_t*>(ws + L.slot_out), T, H, I, E1, K1,
                                 block_m, as_stream(stream)));
 }

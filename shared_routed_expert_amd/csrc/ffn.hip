@@ -8,11 +8,15 @@
 // compute flow, so one structure serves both).
 //
 // gate_up: a[p, i] = silu(g) * u, g/u = dequantised x_q[t] . w13[e] rows i / I+i
-// down:    slot_out[s, h] = bf16( w[s] * dequantised a_q[p] . w2[e] row h )
+// down:    slot_out[s, h] = bf16( w[s] * dequantised a_q[p] . w2[e] row h ), with the
+//          routing weight (times the row's FP8 scale in per-channel mode) taken from
+//          the per-row output scale the quantisation of a writes
 //
-// Each wavefront owns 16 output columns per MFMA tile and all block_m/16 row
-// tiles of its block; operands are loaded straight from global memory in the
-// MFMA's register layout (lane: row/column l & 15, 32 K-bytes at 32 * (l >> 4)).
+// These kernels serve row blocks of 32..128 (block_m == 16 has its own
+// decode-shaped kernels in ffn_decode.hip). Each wavefront owns 16 output
+// columns per MFMA tile and all block_m/16 row tiles of its block; operands are
+// loaded straight from global memory in the MFMA's register layout (lane:
+// row/column l & 15, 32 K-bytes at 32 * (l >> 4)).
 #include "common.hpp"
 
 namespace srmoe {
@@ -28,122 +32,20 @@ __device__ __forceinline__ v8i load32(const uint8_t* p) {
 
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
 
-// Decode-shaped gate_up (block_m == 16): the weights stream from HBM once and each
-// byte feeds a single MFMA, so the kernel is organised for memory-level
-// parallelism. grid: (P_max / 16, I / 16); one workgroup per (row block, 16
-// intermediate columns), its 4 wavefronts splitting K = H four ways, each
-// issuing kPrefetch K-steps of loads ahead of its MFMAs. The partial tiles are
-// summed through LDS in a fixed order, then scaled, passed through SiLU * up
-// and stored as float32.
-template <bool kBlock>
-__global__ void __launch_bounds__(256) gate_up_skinny_kernel(
-    const uint8_t* __restrict__ xq, const float* __restrict__ sx, const uint8_t* __restrict__ w13,
-    const float* __restrict__ s13, const int32_t* __restrict__ sorted,
-    const int32_t* __restrict__ block_expert, const int32_t* __restrict__ num_padded,
-    float* __restrict__ a_out, int T, int H, int I, int K1) {
-  constexpr int kPrefetch = 4;
-  __shared__ float red[4][2][16][17];
-  const int b = blockIdx.x;
-  if (b * 16 >= *num_padded) return;
-  const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int r16 = lane & 15, kq = lane >> 4;
-  const int col0 = blockIdx.y * 16;
-  const int e = block_expert[b];
-  const int sentinel = T * K1;
-  const int HB = H / kGroup;
-  const int nsteps = H / kGroup;
-  const int s0 = wv * nsteps / 4, s1 = (wv + 1) * nsteps / 4;
-
-  const int s_in = sorted[b * 16 + r16];
-  const bool avalid = s_in < sentinel;
-  const uint8_t* arow = xq + (size_t)(avalid ? s_in / K1 : 0) * H + kq * 32;
-  const uint8_t* gp = w13 + ((size_t)e * 2 * I + col0 + r16) * H + kq * 32;
-  const uint8_t* upp = gp + (size_t)I * H;
-  int otok[4];
-  if (kBlock) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int s = sorted[b * 16 + 4 * kq + j];
-      otok[j] = s < sentinel ? s / K1 : -1;
-    }
-  }
-  const size_t sg_base = ((size_t)e * (2 * I / kGroup) + col0 / kGroup) * HB;
-  const size_t su_base = ((size_t)e * (2 * I / kGroup) + (I + col0) / kGroup) * HB;
-
-  const v8i zero8 = {0, 0, 0, 0, 0, 0, 0, 0};
-  const v4f zero4 = {0.f, 0.f, 0.f, 0.f};
-  v4f accg = zero4, accu = zero4;
-  for (int st = s0; st < s1; st += kPrefetch) {
-    v8i A[kPrefetch], G[kPrefetch], U[kPrefetch];
-#pragma unroll
-    for (int j = 0; j < kPrefetch; ++j) {
-      const bool ok = st + j < s1;
-      const size_t k = (size_t)(st + j) * kGroup;
-      A[j] = (ok && avalid) ? load32(arow + k) : zero8;
-      G[j] = ok ? load32(gp + k) : zero8;
-      U[j] = ok ? load32(upp + k) : zero8;
-    }
-#pragma unroll
-    for (int j = 0; j < kPrefetch; ++j) {
-      if (!kBlock) {
-        accg = mfma_16x16x128_fp8(A[j], G[j], accg);
-        accu = mfma_16x16x128_fp8(A[j], U[j], accu);
-      } else if (st + j < s1) {
-        const int kb = st + j;
-        const v4f tg = mfma_16x16x128_fp8(A[j], G[j], zero4);
-        const v4f tu = mfma_16x16x128_fp8(A[j], U[j], zero4);
-        const float swg = s13[sg_base + kb], swu = s13[su_base + kb];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const float sxv = otok[q] >= 0 ? sx[(size_t)otok[q] * HB + kb] : 0.f;
-          accg[q] += tg[q] * (sxv * swg);
-          accu[q] += tu[q] * (sxv * swu);
-        }
-      }
-    }
-  }
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    red[wv][0][4 * kq + q][r16] = accg[q];
-    red[wv][1][4 * kq + q][r16] = accu[q];
-  }
-  __syncthreads();
-  const int row = threadIdx.x >> 4, c = threadIdx.x & 15;
-  float g = red[0][0][row][c], u = red[0][1][row][c];
-#pragma unroll
-  for (int w = 1; w < 4; ++w) {
-    g += red[w][0][row][c];
-    u += red[w][1][row][c];
-  }
-  const int p = b * 16 + row;
-  const int s = sorted[p];
-  float av = 0.f;
-  if (s < sentinel) {
-    if (!kBlock) {
-      const float sxv = sx[s / K1];
-      g = g * sxv * s13[(size_t)e * 2 * I + col0 + c];
-      u = u * sxv * s13[(size_t)e * 2 * I + I + col0 + c];
-    }
-    av = silu(g) * u;
-  }
-  a_out[(size_t)p * I + col0 + c] = av;
-}
-
 // grid: (P_max / block_m, ceil(I / 64)); 4 wavefronts, each 16 intermediate columns
 // (one gate tile and the matching up tile).
 template <int MT, bool kBlock>
 __global__ void __launch_bounds__(256) gate_up_kernel(
     const uint8_t* __restrict__ xq, const float* __restrict__ sx, const uint8_t* __restrict__ w13,
     const float* __restrict__ s13, const int32_t* __restrict__ sorted,
-    const int32_t* __restrict__ block_expert, const int32_t* __restrict__ num_padded,
-    float* __restrict__ a_out, int T, int H, int I, int K1) {
+    const int32_t* __restrict__ block_expert, float* __restrict__ a_out, int T, int H, int I,
+    int K1) {
   constexpr int BM = MT * 16;
   const int b = blockIdx.x;
-  if (b * BM >= *num_padded) return;
+  const int e = block_expert[b];   // -1 past the used rows
   const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int col0 = blockIdx.y * 64 + wv * 16;
-  if (col0 >= I) return;
-  const int e = block_expert[b];
+  if (e < 0 || col0 >= I) return;
   const int r16 = lane & 15, kq = lane >> 4;
   const int sentinel = T * K1;
   const int HB = H / kGroup;
@@ -229,148 +131,172 @@ __global__ void __launch_bounds__(256) gate_up_kernel(
     }
 }
 
-// grid: (P_max / block_m, ceil(H / 256)); 4 wavefronts, each 64 output columns
-// (4 tiles of 16). All loads of a pair of K-steps are issued before its MFMAs.
+// grid: (P_max / block_m, ceil(H / 256)); 4 wavefronts, each 64 output columns as
+// four 16-row MFMA tiles. The weights are the MFMA's A operand (16 rows of w2[e])
+// and the block's quantised a rows its B operand, so D holds [column][token].
+// Inside a wavefront's 64 columns, tile n row r holds column
+// h0 + (r / 4) * 16 + 4 * n + r % 4: then lane (r16, kq) ends with the 16
+// consecutive columns h0 + 16 * kq .. + 15 of token r16 and writes them with two
+// 16-byte stores. All loads of a pair of K-steps are issued ahead of its MFMAs;
+// loads are never predicated per lane (a lane whose K bytes fall past I reads a
+// clamped, valid address and zeroes its B operand), so the compiler's memory
+// waits stay exact; for small row blocks the per-row epilogue data (slot and
+// output scale) is fetched at the start to hide under the weight stream.
 template <int MT, bool kBlock>
 __global__ void __launch_bounds__(256) down_kernel(
     const uint8_t* __restrict__ aq, const float* __restrict__ sa, const uint8_t* __restrict__ w2,
     const float* __restrict__ s2, const int32_t* __restrict__ sorted,
-    const int32_t* __restrict__ block_expert, const int32_t* __restrict__ num_padded,
-    const float* __restrict__ topk_w, uint16_t* __restrict__ slot_out, int T, int H, int I,
-    int K1) {
+    const int32_t* __restrict__ block_expert, const float* __restrict__ row_scale,
+    uint16_t* __restrict__ slot_out, int T, int H, int I, int K1) {
   constexpr int BM = MT * 16;
   constexpr int NT = 4;
   constexpr int KU = 2;   // K-steps per load batch
+  constexpr bool kHoist = MT <= 2;
   const int b = blockIdx.x;
-  if (b * BM >= *num_padded) return;
   const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int h0 = blockIdx.y * 256 + wv * 64;
-  if (h0 >= H) return;
-  const int e = block_expert[b];
   const int r16 = lane & 15, kq = lane >> 4;
+  const int h0 = blockIdx.y * 256 + wv * 64;
+  const int e = block_expert[b];   // -1 past the used rows
+  int srow[MT];
+  float rsc[MT];
+  if (kHoist) {
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+      srow[m] = sorted[b * BM + m * 16 + r16];
+      rsc[m] = row_scale[b * BM + m * 16 + r16];
+    }
+  }
+  if (e < 0 || h0 >= H) return;
   const int sentinel = T * K1;
   const int IB = I / kGroup;
 
-  v4f acc[MT][NT];
-#pragma unroll
-  for (int m = 0; m < MT; ++m)
-#pragma unroll
-    for (int n = 0; n < NT; ++n) acc[m][n] = v4f{0.f, 0.f, 0.f, 0.f};
   const v8i zero8 = {0, 0, 0, 0, 0, 0, 0, 0};
   const v4f zero4 = {0.f, 0.f, 0.f, 0.f};
-  const uint8_t* wrow = w2 + ((size_t)e * H + h0 + r16) * I + kq * 32;
-  const uint8_t* arow = aq + (size_t)(b * BM + r16) * I + kq * 32;
-  for (int k0 = 0; k0 < I; k0 += KU * kGroup) {
-    v8i bw[KU][NT], av[KU][MT];
+  const uint8_t* wbase = w2 + ((size_t)e * H + h0 + (r16 >> 2) * 16 + (r16 & 3)) * I;
+  const uint8_t* abase = aq + (size_t)(b * BM + r16) * I;
+  v8i bw[KU][NT], av[KU][MT];
+  auto load = [&](int k0) {
 #pragma unroll
     for (int u = 0; u < KU; ++u) {
-      const int k = k0 + u * kGroup;
-      const bool in = k + kq * 32 < I;   // I % 32 == 0: a lane's 32 K-bytes are all in or all out
+      const int koff = k0 + u * kGroup + kq * 32;
+      const bool in = koff < I;          // I % 32 == 0: a lane's 32 K-bytes are all in or all out
+      const int kc = in ? koff : I - 32; // clamped, always inside the row
 #pragma unroll
-      for (int n = 0; n < NT; ++n) bw[u][n] = in ? load32(wrow + (size_t)n * 16 * I + k) : zero8;
-#pragma unroll
-      for (int m = 0; m < MT; ++m) av[u][m] = in ? load32(arow + (size_t)m * 16 * I + k) : zero8;
-    }
-#pragma unroll
-    for (int u = 0; u < KU; ++u) {
-      const int k = k0 + u * kGroup;
+      for (int n = 0; n < NT; ++n) bw[u][n] = load32(wbase + (size_t)(4 * n) * I + kc);
 #pragma unroll
       for (int m = 0; m < MT; ++m) {
-        if (!kBlock) {
+        const v8i t = load32(abase + (size_t)m * 16 * I + kc);
+        av[u][m] = in ? t : zero8;       // a zero operand removes the clamped lane's product
+      }
+    }
+  };
+  load(0);
+  float sw[16];   // per-channel scales of this lane's 16 output columns
 #pragma unroll
-          for (int n = 0; n < NT; ++n) acc[m][n] = mfma_16x16x128_fp8(av[u][m], bw[u][n], acc[m][n]);
-        } else if (k < I) {
-          const int kb = k / kGroup;
-          float sr[4];
+  for (int c = 0; c < 16; c += 4) {
+    const float4 v = kBlock ? make_float4(1.f, 1.f, 1.f, 1.f)
+                            : *reinterpret_cast<const float4*>(s2 + (size_t)e * H + h0 + kq * 16 + c);
+    sw[c] = v.x; sw[c + 1] = v.y; sw[c + 2] = v.z; sw[c + 3] = v.w;
+  }
+
+  v4f acc[NT][MT];
 #pragma unroll
-          for (int j = 0; j < 4; ++j) sr[j] = sa[(size_t)(b * BM + m * 16 + 4 * kq + j) * IB + kb];
+  for (int n = 0; n < NT; ++n)
+#pragma unroll
+    for (int m = 0; m < MT; ++m) acc[n][m] = zero4;
+  for (int k0 = 0; k0 < I; k0 += KU * kGroup) {
+    if (k0 > 0) load(k0);
+    __builtin_amdgcn_sched_barrier(0);   // all loads of the batch ahead of its MFMAs
+#pragma unroll
+    for (int u = 0; u < KU; ++u) {
+      const int k = k0 + u * kGroup;
+      if (!kBlock) {
+#pragma unroll
+        for (int n = 0; n < NT; ++n)
+#pragma unroll
+          for (int m = 0; m < MT; ++m) acc[n][m] = mfma_16x16x128_fp8(bw[u][n], av[u][m], acc[n][m]);
+      } else if (k < I) {
+        const int kb = k / kGroup;
+        // a wavefront's 64 columns lie in one 128-column block of w2's scales
+        const float swb = s2[((size_t)e * (H / kGroup) + h0 / kGroup) * IB + kb];
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+          const float sr = sa[(size_t)(b * BM + m * 16 + r16) * IB + kb] * swb;
 #pragma unroll
           for (int n = 0; n < NT; ++n) {
-            const float sw = s2[((size_t)e * (H / kGroup) + (h0 + n * 16) / kGroup) * IB + kb];
-            const v4f t = mfma_16x16x128_fp8(av[u][m], bw[u][n], zero4);
+            const v4f t = mfma_16x16x128_fp8(bw[u][n], av[u][m], zero4);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) acc[m][n][j] += t[j] * (sr[j] * sw);
+            for (int j = 0; j < 4; ++j) acc[n][m][j] += t[j] * sr;
           }
         }
       }
     }
   }
-  float sw[NT];
 #pragma unroll
-  for (int n = 0; n < NT; ++n) sw[n] = kBlock ? 1.f : s2[(size_t)e * H + h0 + n * 16 + r16];
+  for (int m = 0; m < MT; ++m) {
+    const int p = b * BM + m * 16 + r16;
+    const int s = kHoist ? srow[m] : sorted[p];
+    if (s >= sentinel) continue;
+    const float r = kHoist ? rsc[m] : row_scale[p];
+    uint32_t packed[8];
 #pragma unroll
-  for (int m = 0; m < MT; ++m)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int p = b * BM + m * 16 + 4 * kq + j;
-      const int s = sorted[p];
-      if (s >= sentinel) continue;
-      const float rs = (kBlock ? 1.f : sa[p]);
-      const float wgt = topk_w[s];
-#pragma unroll
-      for (int n = 0; n < NT; ++n) {
-        const float y = acc[m][n][j] * rs * sw[n];
-        slot_out[(size_t)s * H + h0 + n * 16 + r16] = f32_to_bf16(y * wgt);
-      }
+    for (int c = 0; c < 16; c += 2) {
+      // column c = 4 * n + j of this lane's 16
+      const float y0 = acc[c >> 2][m][c & 3] * sw[c] * r;
+      const float y1 = acc[(c + 1) >> 2][m][(c + 1) & 3] * sw[c + 1] * r;
+      packed[c >> 1] = (uint32_t)f32_to_bf16(y0) | ((uint32_t)f32_to_bf16(y1) << 16);
     }
+    uint4* dst = reinterpret_cast<uint4*>(slot_out + (size_t)s * H + h0 + kq * 16);
+    dst[0] = make_uint4(packed[0], packed[1], packed[2], packed[3]);
+    dst[1] = make_uint4(packed[4], packed[5], packed[6], packed[7]);
+  }
 }
 
 template <bool kBlock>
 static hipError_t launch_gate_up_t(int block_m, dim3 grid, hipStream_t st, const uint8_t* xq,
                                    const float* sx, const uint8_t* w13, const float* s13,
-                                   const int32_t* sorted, const int32_t* be, const int32_t* np,
-                                   float* a, int T, int H, int I, int K1) {
+                                   const int32_t* sorted, const int32_t* be, float* a, int T, int H,
+                                   int I, int K1) {
   switch (block_m) {
-    case 16: hipLaunchKernelGGL((gate_up_kernel<1, kBlock>), grid, dim3(256), 0, st, xq, sx, w13, s13, sorted, be, np, a, T, H, I, K1); break;
-    case 32: hipLaunchKernelGGL((gate_up_kernel<2, kBlock>), grid, dim3(256), 0, st, xq, sx, w13, s13, sorted, be, np, a, T, H, I, K1); break;
-    case 64: hipLaunchKernelGGL((gate_up_kernel<4, kBlock>), grid, dim3(256), 0, st, xq, sx, w13, s13, sorted, be, np, a, T, H, I, K1); break;
-    default: hipLaunchKernelGGL((gate_up_kernel<8, kBlock>), grid, dim3(256), 0, st, xq, sx, w13, s13, sorted, be, np, a, T, H, I, K1); break;
+    case 32: hipLaunchKernelGGL((gate_up_kernel<2, kBlock>), grid, dim3(256), 0, st, xq, sx, w13, s13, sorted, be, a, T, H, I, K1); break;
+    case 64: hipLaunchKernelGGL((gate_up_kernel<4, kBlock>), grid, dim3(256), 0, st, xq, sx, w13, s13, sorted, be, a, T, H, I, K1); break;
+    default: hipLaunchKernelGGL((gate_up_kernel<8, kBlock>), grid, dim3(256), 0, st, xq, sx, w13, s13, sorted, be, a, T, H, I, K1); break;
   }
   return hipGetLastError();
 }
 
+// block_m 32..128 (block_m 16 uses launch_gate_up_decode).
 hipError_t launch_gate_up(const uint8_t* xq, const float* sx, const uint8_t* w13, const float* s13,
-                          bool block, const int32_t* sorted, const int32_t* block_expert,
-                          const int32_t* num_padded, float* a, int T, int H, int I, int E1, int K1,
-                          int block_m, hipStream_t stream) {
+                          bool block, const int32_t* sorted, const int32_t* block_expert, float* a,
+                          int T, int H, int I, int E1, int K1, int block_m, hipStream_t stream) {
   const int P_max = (int)sorted_capacity(T, K1, E1, block_m);
-  if (block_m == 16) {
-    const dim3 grid(P_max / 16, I / 16);
-    if (block)
-      hipLaunchKernelGGL(gate_up_skinny_kernel<true>, grid, dim3(256), 0, stream, xq, sx, w13, s13,
-                         sorted, block_expert, num_padded, a, T, H, I, K1);
-    else
-      hipLaunchKernelGGL(gate_up_skinny_kernel<false>, grid, dim3(256), 0, stream, xq, sx, w13, s13,
-                         sorted, block_expert, num_padded, a, T, H, I, K1);
-    return hipGetLastError();
-  }
   const dim3 grid(P_max / block_m, (I + 63) / 64);
-  return block ? launch_gate_up_t<true>(block_m, grid, stream, xq, sx, w13, s13, sorted, block_expert, num_padded, a, T, H, I, K1)
-               : launch_gate_up_t<false>(block_m, grid, stream, xq, sx, w13, s13, sorted, block_expert, num_padded, a, T, H, I, K1);
+  return block ? launch_gate_up_t<true>(block_m, grid, stream, xq, sx, w13, s13, sorted, block_expert, a, T, H, I, K1)
+               : launch_gate_up_t<false>(block_m, grid, stream, xq, sx, w13, s13, sorted, block_expert, a, T, H, I, K1);
 }
 
 template <bool kBlock>
 static hipError_t launch_down_t(int block_m, dim3 grid, hipStream_t st, const uint8_t* aq,
                                 const float* sa, const uint8_t* w2, const float* s2,
-                                const int32_t* sorted, const int32_t* be, const int32_t* np,
-                                const float* tw, uint16_t* so, int T, int H, int I, int K1) {
+                                const int32_t* sorted, const int32_t* be, const float* rs,
+                                uint16_t* so, int T, int H, int I, int K1) {
   switch (block_m) {
-    case 16: hipLaunchKernelGGL((down_kernel<1, kBlock>), grid, dim3(256), 0, st, aq, sa, w2, s2, sorted, be, np, tw, so, T, H, I, K1); break;
-    case 32: hipLaunchKernelGGL((down_kernel<2, kBlock>), grid, dim3(256), 0, st, aq, sa, w2, s2, sorted, be, np, tw, so, T, H, I, K1); break;
-    case 64: hipLaunchKernelGGL((down_kernel<4, kBlock>), grid, dim3(256), 0, st, aq, sa, w2, s2, sorted, be, np, tw, so, T, H, I, K1); break;
-    default: hipLaunchKernelGGL((down_kernel<8, kBlock>), grid, dim3(256), 0, st, aq, sa, w2, s2, sorted, be, np, tw, so, T, H, I, K1); break;
+    case 16: hipLaunchKernelGGL((down_kernel<1, kBlock>), grid, dim3(256), 0, st, aq, sa, w2, s2, sorted, be, rs, so, T, H, I, K1); break;
+    case 32: hipLaunchKernelGGL((down_kernel<2, kBlock>), grid, dim3(256), 0, st, aq, sa, w2, s2, sorted, be, rs, so, T, H, I, K1); break;
+    case 64: hipLaunchKernelGGL((down_kernel<4, kBlock>), grid, dim3(256), 0, st, aq, sa, w2, s2, sorted, be, rs, so, T, H, I, K1); break;
+    default: hipLaunchKernelGGL((down_kernel<8, kBlock>), grid, dim3(256), 0, st, aq, sa, w2, s2, sorted, be, rs, so, T, H, I, K1); break;
   }
   return hipGetLastError();
 }
 
 hipError_t launch_down(const uint8_t* aq, const float* sa, const uint8_t* w2, const float* s2,
                        bool block, const int32_t* sorted, const int32_t* block_expert,
-                       const int32_t* num_padded, const float* topk_w, uint16_t* slot_out, int T,
-                       int H, int I, int E1, int K1, int block_m, hipStream_t stream) {
+                       const float* row_scale, uint16_t* slot_out, int T, int H, int I, int E1,
+                       int K1, int block_m, hipStream_t stream) {
   const int P_max = (int)sorted_capacity(T, K1, E1, block_m);
   const dim3 grid(P_max / block_m, (H + 255) / 256);
-  return block ? launch_down_t<true>(block_m, grid, stream, aq, sa, w2, s2, sorted, block_expert, num_padded, topk_w, slot_out, T, H, I, K1)
-               : launch_down_t<false>(block_m, grid, stream, aq, sa, w2, s2, sorted, block_expert, num_padded, topk_w, slot_out, T, H, I, K1);
+  return block ? launch_down_t<true>(block_m, grid, stream, aq, sa, w2, s2, sorted, block_expert, row_scale, slot_out, T, H, I, K1)
+               : launch_down_t<false>(block_m, grid, stream, aq, sa, w2, s2, sorted, block_expert, row_scale, slot_out, T, H, I, K1);
 }
 
 // out[t, :] = bf16( sum_k slot_out[t*K1 + k, :] ), float32 in slot order. 8 columns per thread.

@@ -1,0 +1,156 @@
+// Decode-shaped expert GEMMs (block_m == 16) of the fused MoE layer.
+//
+// With few tokens per expert every weight byte feeds one MFMA, so these
+// kernels are organised around streaming the expert weights from HBM: many
+// short workgroups with several K steps of loads in flight per wavefront.
+//
+// Operand layout as everywhere here: lane l takes row/column l & 15 and the 32
+// K-bytes at 32 * (l >> 4) of each 128-byte K step (one K step per MFMA).
+// (Giving each lane a longer contiguous run of K was measured slower: every
+// load instruction then touches four times as many cache lines.)
+//
+// gate_up: grid (P_max/16, I/16); the 4 wavefronts take contiguous quarters of
+//          K = H and issue kPrefetch steps of loads ahead of their MFMAs; the
+//          partial tiles are summed through LDS in a fixed order; a = silu(g)*u
+//          as float32. The epilogue's row data is fetched at the start so its
+//          latency hides under the weight stream.
+// (The down GEMM for these blocks is the generic kernel in ffn.hip with one row
+// tile; quantising a inside its prologue was measured slower than one separate
+// quantisation pass, because every column tile then repeats the work.)
+#include "common.hpp"
+
+namespace srmoe {
+
+__device__ __forceinline__ v8i ld32(const uint8_t* p) {
+  const uint4 lo = *reinterpret_cast<const uint4*>(p);
+  const uint4 hi = *reinterpret_cast<const uint4*>(p + 16);
+  v8i r;
+  r[0] = lo.x; r[1] = lo.y; r[2] = lo.z; r[3] = lo.w;
+  r[4] = hi.x; r[5] = hi.y; r[6] = hi.z; r[7] = hi.w;
+  return r;
+}
+
+__device__ __forceinline__ float silu_f(float z) { return z / (1.0f + __expf(-z)); }
+
+template <bool kBlock>
+__global__ void __launch_bounds__(256) gate_up_decode_kernel(
+    const uint8_t* __restrict__ xq, const float* __restrict__ sx, const uint8_t* __restrict__ w13,
+    const float* __restrict__ s13, const int32_t* __restrict__ sorted,
+    const int32_t* __restrict__ block_expert, float* __restrict__ a_out, int T, int H, int I,
+    int K1) {
+  constexpr int kPrefetch = 5;
+  __shared__ float red[4][2][16][17];
+  const int b = blockIdx.x;
+  const int e = block_expert[b];   // -1 past the used rows
+  const int erow = threadIdx.x >> 4, ec = threadIdx.x & 15;   // epilogue element of this thread
+  const int s_epi = sorted[b * 16 + erow];
+  if (e < 0) return;
+  const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int r16 = lane & 15, kq = lane >> 4;
+  const int col0 = blockIdx.y * 16;
+  const int sentinel = T * K1;
+  const int HB = H / kGroup;
+  const int nsteps = H / kGroup;
+  const int s0 = wv * nsteps / 4, s1 = (wv + 1) * nsteps / 4;
+
+  // No load below is predicated per lane, so the compiler's memory waits stay exact:
+  // padding rows read token 0 (their outputs are discarded) and the unused slots of
+  // the last prefetch batch re-read the wavefront's last step.
+  const int s_in = sorted[b * 16 + r16];
+  const uint8_t* arow = xq + (size_t)(s_in < sentinel ? s_in / K1 : 0) * H + kq * 32;
+  const uint8_t* gp = w13 + ((size_t)e * 2 * I + col0 + r16) * H + kq * 32;
+  const uint8_t* upp = gp + (size_t)I * H;
+  int otok[4] = {0, 0, 0, 0};
+  bool oval[4] = {false, false, false, false};
+  if (kBlock) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int s = sorted[b * 16 + 4 * kq + q];
+      oval[q] = s < sentinel;
+      otok[q] = oval[q] ? s / K1 : 0;
+    }
+  }
+  const size_t sg_base = ((size_t)e * (2 * I / kGroup) + col0 / kGroup) * HB;
+  const size_t su_base = ((size_t)e * (2 * I / kGroup) + (I + col0) / kGroup) * HB;
+  const v4f zero4 = {0.f, 0.f, 0.f, 0.f};
+  v4f accg = zero4, accu = zero4;
+  float e_sx = 0.f, e_sg = 1.f, e_su = 1.f;
+  if (!kBlock) {
+    e_sg = s13[(size_t)e * 2 * I + col0 + ec];
+    e_su = s13[(size_t)e * 2 * I + I + col0 + ec];
+    e_sx = sx[s_epi < sentinel ? s_epi / K1 : 0];
+  }
+
+  const v8i zero8 = {0, 0, 0, 0, 0, 0, 0, 0};
+  for (int st = s0; st < s1; st += kPrefetch) {
+    v8i A[kPrefetch], G[kPrefetch], U[kPrefetch];
+#pragma unroll
+    for (int j = 0; j < kPrefetch; ++j) {
+      const size_t k = (size_t)min(st + j, s1 - 1) * kGroup;
+      const v8i t = ld32(arow + k);
+      A[j] = st + j < s1 ? t : zero8;   // a repeated step contributes nothing
+      G[j] = ld32(gp + k);
+      U[j] = ld32(upp + k);
+    }
+    // keep every load of the batch ahead of its MFMAs (the scheduler would otherwise
+    // interleave them and wait on each step in turn)
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int j = 0; j < kPrefetch; ++j) {
+      if (!kBlock) {
+        accg = mfma_16x16x128_fp8(A[j], G[j], accg);
+        accu = mfma_16x16x128_fp8(A[j], U[j], accu);
+      } else if (st + j < s1) {
+        const int kb = st + j;
+        const v4f tg = mfma_16x16x128_fp8(A[j], G[j], zero4);
+        const v4f tu = mfma_16x16x128_fp8(A[j], U[j], zero4);
+        const float swg = s13[sg_base + kb], swu = s13[su_base + kb];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float sxl = sx[(size_t)otok[q] * HB + kb];
+          const float sxv = oval[q] ? sxl : 0.f;
+          accg[q] += tg[q] * (sxv * swg);
+          accu[q] += tu[q] * (sxv * swu);
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    red[wv][0][4 * kq + q][r16] = accg[q];
+    red[wv][1][4 * kq + q][r16] = accu[q];
+  }
+  __syncthreads();
+  float g = red[0][0][erow][ec], u = red[0][1][erow][ec];
+#pragma unroll
+  for (int w = 1; w < 4; ++w) {
+    g += red[w][0][erow][ec];
+    u += red[w][1][erow][ec];
+  }
+  float av = 0.f;
+  if (s_epi < sentinel) {
+    if (!kBlock) {
+      g = g * e_sx * e_sg;
+      u = u * e_sx * e_su;
+    }
+    av = silu_f(g) * u;
+  }
+  a_out[(size_t)(b * 16 + erow) * I + col0 + ec] = av;
+}
+
+hipError_t launch_gate_up_decode(const uint8_t* xq, const float* sx, const uint8_t* w13,
+                                 const float* s13, bool block, const int32_t* sorted,
+                                 const int32_t* block_expert, float* a, int T, int H, int I, int E1,
+                                 int K1, hipStream_t stream) {
+  const int P_max = (int)sorted_capacity(T, K1, E1, 16);
+  const dim3 grid(P_max / 16, I / 16);
+  if (block)
+    hipLaunchKernelGGL(gate_up_decode_kernel<true>, grid, dim3(256), 0, stream, xq, sx, w13, s13,
+                       sorted, block_expert, a, T, H, I, K1);
+  else
+    hipLaunchKernelGGL(gate_up_decode_kernel<false>, grid, dim3(256), 0, stream, xq, sx, w13, s13,
+                       sorted, block_expert, a, T, H, I, K1);
+  return hipGetLastError();
+}
+
+}  // namespace srmoe

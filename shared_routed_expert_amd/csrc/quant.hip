@@ -35,16 +35,30 @@ __global__ void __launch_bounds__(256) quant_x_kernel(const uint16_t* __restrict
   const uint16_t* row = x + (size_t)t * H;
   uint8_t* qrow = xq + (size_t)t * H;
   if (!kBlock) {
+    // one pass: H <= 8192 keeps the row in registers (8 stripes of 4 values per thread)
+    constexpr int kMaxStripes = 8;
+    float4 v[kMaxStripes];
     float amax = 0.0f;
-    for (int h = tid * 4; h < H; h += 1024) amax = fmaxf(amax, amax4(load_bf16x4(row + h)));
+#pragma unroll
+    for (int i = 0; i < kMaxStripes; ++i) {
+      const int h = i * 1024 + tid * 4;
+      v[i] = h < H ? load_bf16x4(row + h) : make_float4(0.f, 0.f, 0.f, 0.f);
+      amax = fmaxf(amax, amax4(v[i]));
+    }
+    for (int h = kMaxStripes * 1024 + tid * 4; h < H; h += 1024) amax = fmaxf(amax, amax4(load_bf16x4(row + h)));
     amax = wave_max(amax);
     if (lane == 0) red[wv] = amax;
     __syncthreads();
     const float scale = fp8_scale(fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3])));
     if (tid == 0) sx[t] = scale;
-    for (int h = tid * 4; h < H; h += 1024) {
-      const float4 v = load_bf16x4(row + h);
-      *reinterpret_cast<uint32_t*>(qrow + h) = encode4(v.x, v.y, v.z, v.w, scale);
+#pragma unroll
+    for (int i = 0; i < kMaxStripes; ++i) {
+      const int h = i * 1024 + tid * 4;
+      if (h < H) *reinterpret_cast<uint32_t*>(qrow + h) = encode4(v[i].x, v[i].y, v[i].z, v[i].w, scale);
+    }
+    for (int h = kMaxStripes * 1024 + tid * 4; h < H; h += 1024) {
+      const float4 w = load_bf16x4(row + h);
+      *reinterpret_cast<uint32_t*>(qrow + h) = encode4(w.x, w.y, w.z, w.w, scale);
     }
   } else {
     // 128-wide groups are 32 consecutive threads; H % 128 == 0 keeps every group whole.
@@ -59,32 +73,63 @@ __global__ void __launch_bounds__(256) quant_x_kernel(const uint16_t* __restrict
   }
 }
 
-// a [P,I] float32 -> aq [P,I] e4m3, sa [P] or [P,I/128], for rows p < num_padded.
-// One 256-thread workgroup per 16 rows, 16 threads (one DPP row) per sorted row;
-// each thread takes 2 consecutive values per 32-wide stripe.
+// a [P,I] float32 -> aq [P,I] e4m3, sa [P] or [P,I/128].
+// It also writes each sorted row's output scale for the down GEMM: the row's
+// routing weight topk_w[s] (0 for padding rows), times the row's FP8 scale in
+// per-channel mode. One 256-thread workgroup per 16 rows, 16 threads (one DPP
+// row) per sorted row; each thread takes 2 consecutive values per 32-wide stripe.
 template <bool kBlock>
 __global__ void __launch_bounds__(256) quant_a_kernel(const float* __restrict__ a, int I,
-                                                      const int32_t* __restrict__ num_padded,
-                                                      uint8_t* __restrict__ aq, float* __restrict__ sa) {
-  if (blockIdx.x * 16 >= *num_padded) return;   // num_padded is a multiple of 16
+                                                      const int32_t* __restrict__ sorted,
+                                                      const float* __restrict__ topk_w, int sentinel,
+                                                      uint8_t* __restrict__ aq, float* __restrict__ sa,
+                                                      float* __restrict__ row_scale) {
+  // Every row up to the sort capacity is processed: rows past the used blocks hold
+  // stale data whose codes no GEMM reads, and skipping the block check saves a
+  // dependent load at the start.
   const int p = blockIdx.x * 16 + (threadIdx.x >> 4);
   const int part = threadIdx.x & 15;
   const float* row = a + (size_t)p * I;
   uint8_t* qrow = aq + (size_t)p * I;
+  float wgt = 0.f;
+  if (part == 0) {
+    const int s = sorted[p];
+    if (s < sentinel) wgt = topk_w[s];
+  }
   if (!kBlock) {
+    // one pass for I <= 512 (16 stripes of 2 values per thread), else two
+    constexpr int kMaxStripes = 16;
+    float2 v[kMaxStripes];
     float amax = 0.0f;
-    for (int i = part * 2; i < I; i += 32) {
-      const float2 v = *reinterpret_cast<const float2*>(row + i);
-      amax = fmaxf(amax, fmaxf(fabsf(v.x), fabsf(v.y)));
+#pragma unroll
+    for (int j = 0; j < kMaxStripes; ++j) {
+      const int i = j * 32 + part * 2;
+      v[j] = i < I ? *reinterpret_cast<const float2*>(row + i) : make_float2(0.f, 0.f);
+      amax = fmaxf(amax, fmaxf(fabsf(v[j].x), fabsf(v[j].y)));
+    }
+    for (int i = kMaxStripes * 32 + part * 2; i < I; i += 32) {
+      const float2 w = *reinterpret_cast<const float2*>(row + i);
+      amax = fmaxf(amax, fmaxf(fabsf(w.x), fabsf(w.y)));
     }
     const float scale = fp8_scale(row16_max(amax));
-    if (part == 0) sa[p] = scale;
-    for (int i = part * 2; i < I; i += 32) {
-      const float2 v = *reinterpret_cast<const float2*>(row + i);
+    if (part == 0) {
+      sa[p] = scale;
+      row_scale[p] = wgt * scale;
+    }
+#pragma unroll
+    for (int j = 0; j < kMaxStripes; ++j) {
+      const int i = j * 32 + part * 2;
+      if (i < I)
+        *reinterpret_cast<uint16_t*>(qrow + i) =
+            (uint16_t)(e4m3_encode(__fdiv_rn(v[j].x, scale)) | (e4m3_encode(__fdiv_rn(v[j].y, scale)) << 8));
+    }
+    for (int i = kMaxStripes * 32 + part * 2; i < I; i += 32) {
+      const float2 w = *reinterpret_cast<const float2*>(row + i);
       *reinterpret_cast<uint16_t*>(qrow + i) =
-          (uint16_t)(e4m3_encode(__fdiv_rn(v.x, scale)) | (e4m3_encode(__fdiv_rn(v.y, scale)) << 8));
+          (uint16_t)(e4m3_encode(__fdiv_rn(w.x, scale)) | (e4m3_encode(__fdiv_rn(w.y, scale)) << 8));
     }
   } else {
+    if (part == 0) row_scale[p] = wgt;
     for (int g = 0; g < I; g += kGroup) {
       float2 v[4];
       float amax = 0.0f;
@@ -113,13 +158,14 @@ hipError_t launch_quant_x(const uint16_t* x, int T, int H, bool block, uint8_t* 
   return hipGetLastError();
 }
 
-hipError_t launch_quant_a(const float* a, int P_max, int I, bool block, const int32_t* num_padded,
-                          uint8_t* aq, float* sa, hipStream_t stream) {
+hipError_t launch_quant_a(const float* a, int P_max, int I, bool block, const int32_t* sorted,
+                          const float* topk_w, int sentinel, uint8_t* aq, float* sa, float* row_scale,
+                          hipStream_t stream) {
   const dim3 grid(P_max / 16), blk(256);
   if (block)
-    hipLaunchKernelGGL(quant_a_kernel<true>, grid, blk, 0, stream, a, I, num_padded, aq, sa);
+    hipLaunchKernelGGL(quant_a_kernel<true>, grid, blk, 0, stream, a, I, sorted, topk_w, sentinel, aq, sa, row_scale);
   else
-    hipLaunchKernelGGL(quant_a_kernel<false>, grid, blk, 0, stream, a, I, num_padded, aq, sa);
+    hipLaunchKernelGGL(quant_a_kernel<false>, grid, blk, 0, stream, a, I, sorted, topk_w, sentinel, aq, sa, row_scale);
   return hipGetLastError();
 }
 

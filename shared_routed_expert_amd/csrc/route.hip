@@ -57,15 +57,21 @@ __global__ void __launch_bounds__(256) route_topk_plus_shared_kernel(
   }
   // Renormalised softmax over the selected logits: p_k / sum_j p_j with the full
   // softmax denominator cancelling; exponents are taken relative to the top logit.
-  float denom = 0.0f;
+  // Lane k < K takes the exponent of slot k; the denominator is summed in slot order.
+  float mine = 0.0f, denom = 0.0f;
 #pragma unroll
-  for (int k = 0; k < 15; ++k)
-    if (k < K) denom += expf(sel_val[k] - sel_val[0]);
+  for (int k = 0; k < 15; ++k) {
+    if (k < K) {
+      const float p = expf(sel_val[k] - sel_val[0]);
+      denom += p;
+      if (lane == k) mine = p;
+    }
+  }
 #pragma unroll
   for (int k = 0; k < 15; ++k) {
     if (k < K && lane == k) {
       ids[(size_t)t * K1 + k] = sel_id[k];
-      w[(size_t)t * K1 + k] = __fdiv_rn(expf(sel_val[k] - sel_val[0]), denom);
+      w[(size_t)t * K1 + k] = __fdiv_rn(mine, denom);
     }
   }
   if (lane == K) {

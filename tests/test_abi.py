@@ -63,7 +63,7 @@ def test_capacity_and_workspace_sizes(L):
     off = L.moe_ffn_workspace_offsets(64, 5120, 192, 161, 9, 16, 0)
     assert off["slot_out"] == 0
     assert off["total"] == L.moe_ffn_workspace_bytes(64, 5120, 192, 161, 9, 16, 0)
-    keys = ["slot_out", "xq", "sx", "a", "aq", "sa", "total"]
+    keys = ["slot_out", "xq", "sx", "a", "aq", "sa", "rs", "total"]
     vals = [off[k] for k in keys]
     assert vals == sorted(vals) and all(v % 256 == 0 for v in vals)
     assert off["xq"] >= 64 * 9 * 5120 * 2
