@@ -124,7 +124,10 @@ def main():
     layer = FusedMoE(cfg.T, cfg.H, cfg.I, cfg.E, cfg.K, bm, weights[0].scale_mode, device=dev)
     stream = torch.cuda.current_stream()
 
-    def step(i):
+    def step(i):   # the whole layer through one C call (moe_layer_forward)
+        layer.forward_fused(x, logits, weights[i % len(weights)], 1.0, stream)
+
+    def step_four_calls(i):   # the same layer as the four separate C calls
         layer.forward(x, logits, weights[i % len(weights)], 1.0, stream)
 
     log(f"bench: warmup {args.warmup} steps")
@@ -143,7 +146,16 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = ev0.elapsed_time(ev1) / args.steps
-    log(f"bench: {ms_per_step * 1e3:.1f} us/step (wall {wall * 1e3 / args.steps:.1f} us/step)")
+    log(f"bench: {ms_per_step * 1e3:.1f} us/step on the GPU, {wall * 1e6 / args.steps:.1f} us/step wall-clock")
+
+    # The same K steps through the four separate calls, for comparison.
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for i in range(args.steps):
+        step_four_calls(i)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    four_ms = ev0.elapsed_time(ev1) / args.steps
 
     # Timed region 2: the same steps with HIP events between the stages (same stream),
     # giving each stage's average duration, the dominant kernel's included.
@@ -205,7 +217,9 @@ def main():
                   "hbm_frac": round(layer_bytes / step_s / 1e9 / HBM_PEAK_GBS, 4),
                   "alg_TFLOPs": round(flops / step_s / 1e12, 2),
                   "fp8_frac": round(flops / step_s / 1e12 / FP8_PEAK_TFLOPS, 4),
-                  "stage_us": {k: round(v, 2) for k, v in stage_us.items()}},
+                  "stage_us": {k: round(v, 2) for k, v in stage_us.items()},
+                  "entry_point": "moe_layer_forward",
+                  "four_call_ms_per_step": round(four_ms, 5)},
     }
     if not args.no_cpu_baseline:
         log("bench: timing the CPU oracle")

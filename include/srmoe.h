@@ -149,6 +149,21 @@ int moe_ffn_down(const uint8_t* w2, const float* s2, int scale_mode, int T, int 
 int moe_combine(int T, int K1, int H, const void* workspace, size_t ws_bytes, uint16_t* out,
                 void* stream);
 
+/* ---------------------------------------------------------------------------
+ * The whole layer in one call: steps 1-4 with the arguments of the four calls
+ * above (K routed slots, E routed experts; K1 = K+1, E1 = E+1) and the same
+ * outputs, bit for bit. The routing and the FP8 quantisation of x do not depend
+ * on each other and share one launch, so the layer takes one launch fewer than
+ * the four calls. align_ws/ffn_ws as for moe_align_by_expert/moe_fused_ffn.
+ * ------------------------------------------------------------------------- */
+int moe_layer_forward(const uint16_t* x, const float* logits, const uint8_t* w13, const float* s13,
+                      const uint8_t* w2, const float* s2, int scale_mode, int T, int H, int I, int E,
+                      int K, float shared_weight, int block_m, int32_t* topk_ids, float* topk_w,
+                      int32_t* sorted_slot_ids, int32_t* block_expert, int32_t* expert_counts,
+                      int32_t* expert_offsets, int32_t* num_padded, void* align_ws,
+                      size_t align_ws_bytes, void* ffn_ws, size_t ffn_ws_bytes, uint16_t* out,
+                      void* stream);
+
 /* Host helpers. */
 size_t moe_sorted_capacity(int T, int K1, int E1, int block_m); /* P_max, rows */
 size_t moe_align_workspace_bytes(int T, int K1, int E1);

@@ -39,6 +39,7 @@ def _load():
         "moe_ffn_gate_up": ([P, P, I, I, I, I, I, I, I, P, P, P, P, Z, P], I),
         "moe_ffn_down": ([P, P, I, I, I, I, I, I, I, P, P, P, P, P, Z, P], I),
         "moe_combine": ([I, I, I, P, Z, P, P], I),
+        "moe_layer_forward": ([P, P, P, P, P, P, I, I, I, I, I, I, F, I, P, P, P, P, P, P, P, P, Z, P, Z, P, P], I),
         "moe_sorted_capacity": ([I, I, I, I], Z),
         "moe_align_workspace_bytes": ([I, I, I], Z),
         "moe_ffn_workspace_bytes": ([I, I, I, I, I, I, I], Z),
@@ -56,7 +57,7 @@ def _load():
 lib = _load()
 
 EXPORTED = ("moe_route_topk_plus_shared", "moe_align_by_expert", "moe_fused_ffn", "moe_ffn_quant_x",
-            "moe_ffn_gate_up", "moe_ffn_down", "moe_combine", "moe_sorted_capacity",
+            "moe_ffn_gate_up", "moe_ffn_down", "moe_combine", "moe_layer_forward", "moe_sorted_capacity",
             "moe_align_workspace_bytes", "moe_ffn_workspace_bytes", "moe_ffn_workspace_offsets",
             "srmoe_status_string",
             "srmoe_last_hip_error")
@@ -153,3 +154,16 @@ def moe_ffn_down(w2, s2, scale_mode, T, H, I, E1, K1, block_m, sorted_slot_ids, 
 def moe_combine(T, K1, H, workspace, ws_bytes, out, stream=None, check=True):
     st = lib.moe_combine(T, K1, H, _ptr(workspace), ws_bytes, _ptr(out), _stream(stream))
     return _check("moe_combine", st) if check else st
+
+
+def moe_layer_forward(x, logits, w13, s13, w2, s2, scale_mode, T, H, I, E, K, shared_weight, block_m,
+                      topk_ids, topk_w, sorted_slot_ids, block_expert, expert_counts, expert_offsets,
+                      num_padded, align_ws, align_ws_bytes, ffn_ws, ffn_ws_bytes, out, stream=None,
+                      check=True):
+    st = lib.moe_layer_forward(_ptr(x), _ptr(logits), _ptr(w13), _ptr(s13), _ptr(w2), _ptr(s2),
+                               scale_mode, T, H, I, E, K, shared_weight, block_m, _ptr(topk_ids),
+                               _ptr(topk_w), _ptr(sorted_slot_ids), _ptr(block_expert),
+                               _ptr(expert_counts), _ptr(expert_offsets), _ptr(num_padded),
+                               _ptr(align_ws), align_ws_bytes, _ptr(ffn_ws), ffn_ws_bytes, _ptr(out),
+                               _stream(stream))
+    return _check("moe_layer_forward", st) if check else st

@@ -22,6 +22,8 @@ hipError_t launch_combine(const uint16_t*, int, int, int, uint16_t*, hipStream_t
 hipError_t launch_gate_up_decode(const uint8_t*, const float*, const uint8_t*, const float*, bool,
                                  const int32_t*, const int32_t*, float*, int, int, int, int, int,
                                  hipStream_t);
+hipError_t launch_layer_front(const float*, int, int, int, float, int32_t*, float*, const uint16_t*,
+                              int, bool, uint8_t*, float*, hipStream_t);
 }  // namespace srmoe
 
 using namespace srmoe;
@@ -253,6 +255,46 @@ int moe_fused_ffn(const uint16_t* x, const uint8_t* w13, const float* s13, const
   if (st != SRMOE_OK) return st;
   return moe_ffn_down(w2, s2, scale_mode, T, H, I, E1, K1, block_m, sorted_slot_ids, block_expert,
                       num_padded, topk_w, workspace, ws_bytes, stream);
+}
+
+int moe_layer_forward(const uint16_t* x, const float* logits, const uint8_t* w13, const float* s13,
+                      const uint8_t* w2, const float* s2, int scale_mode, int T, int H, int I, int E,
+                      int K, float shared_weight, int block_m, int32_t* topk_ids, float* topk_w,
+                      int32_t* sorted_slot_ids, int32_t* block_expert, int32_t* expert_counts,
+                      int32_t* expert_offsets, int32_t* num_padded, void* align_ws,
+                      size_t align_ws_bytes, void* ffn_ws, size_t ffn_ws_bytes, uint16_t* out,
+                      void* stream) {
+  // every check of the four calls, before anything is launched
+  if (T < 0 || T > kMaxT || E < 1 || K < 0) return SRMOE_ERR_INVALID_ARG;
+  if (E > 255 || K > E || K > 15) return SRMOE_ERR_UNSUPPORTED;
+  const int E1 = E + 1, K1 = K + 1;
+  int st = check_ffn_dims(scale_mode, T, H, I, E1, K1, block_m);
+  if (st != SRMOE_OK) return st;
+  if (T == 0) return SRMOE_OK;
+  const void* ptrs[] = {x, logits, w13, s13, w2, s2, topk_ids, topk_w, sorted_slot_ids, block_expert,
+                        expert_counts, expert_offsets, num_padded, align_ws, ffn_ws, out};
+  for (const void* p : ptrs)
+    if (!p || !aligned16(p)) return SRMOE_ERR_INVALID_ARG;
+  if (align_ws_bytes < moe_align_workspace_bytes(T, K1, E1)) return SRMOE_ERR_WORKSPACE;
+  const FfnLayout L = ffn_layout(T, H, I, E1, K1, block_m, scale_mode);
+  if (ffn_ws_bytes < L.total) return SRMOE_ERR_WORKSPACE;
+  char* ws = static_cast<char*>(ffn_ws);
+  const bool blk = scale_mode == SRMOE_SCALE_BLOCK128;
+  hipStream_t sm = as_stream(stream);
+  st = hip_status(launch_layer_front(logits, T, E, K, shared_weight, topk_ids, topk_w, x, H, blk,
+                                     reinterpret_cast<uint8_t*>(ws + L.xq),
+                                     reinterpret_cast<float*>(ws + L.sx), sm));
+  if (st != SRMOE_OK) return st;
+  st = moe_align_by_expert(topk_ids, T, K1, E1, block_m, sorted_slot_ids, block_expert, expert_counts,
+                           expert_offsets, num_padded, align_ws, align_ws_bytes, stream);
+  if (st != SRMOE_OK) return st;
+  st = moe_ffn_gate_up(w13, s13, scale_mode, T, H, I, E1, K1, block_m, sorted_slot_ids, block_expert,
+                       num_padded, ffn_ws, ffn_ws_bytes, stream);
+  if (st != SRMOE_OK) return st;
+  st = moe_ffn_down(w2, s2, scale_mode, T, H, I, E1, K1, block_m, sorted_slot_ids, block_expert,
+                    num_padded, topk_w, ffn_ws, ffn_ws_bytes, stream);
+  if (st != SRMOE_OK) return st;
+  return moe_combine(T, K1, H, ffn_ws, ffn_ws_bytes, out, stream);
 }
 
 int moe_combine(int T, int K1, int H, const void* workspace, size_t ws_bytes, uint16_t* out,

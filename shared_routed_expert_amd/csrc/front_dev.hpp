@@ -1,0 +1,313 @@
+// Device code shared by the routing, align and x-quantisation kernels and by the
+// fused front of moe_layer_forward.
+#pragma once
+#include "common.hpp"
+
+namespace srmoe {
+
+// ----------------------------------------------------------------------------- routing
+// Order-preserving map of a finite float to uint32 (-0 is folded into +0, so
+// equal values compare equal and the id decides).
+__device__ __forceinline__ uint32_t ordered_key(float f) {
+  uint32_t u = __float_as_uint(f == 0.0f ? 0.0f : f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float key_to_float(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+
+// Route token t with the 64 lanes of the caller's wavefront: the K routed experts
+// with the largest logits in the order (logit desc, id asc), weights
+// p_k / sum_{j in top-K} p_j (the full softmax denominator cancels; exponents are
+// taken relative to the top logit), then the shared expert E in slot K with
+// coefficient shared_weight. Each lane holds the logits of experts lane, lane+64,
+// ... (E <= 255); each of the K rounds is a local max and a DPP wave reduction of a
+// 64-bit key (ordered logit, 255 - id). ids/w are written to global memory;
+// lds_ids (if not null) gets a copy of the ids.
+__device__ __forceinline__ void route_token_wave(const float* __restrict__ logits, int t, int E, int K,
+                                                 float shared_weight, int32_t* __restrict__ ids,
+                                                 float* __restrict__ w, int* lds_ids) {
+  const int lane = threadIdx.x & 63;
+  const int K1 = K + 1;
+  uint64_t key[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int e = lane + 64 * j;
+    key[j] = (e < E) ? ((uint64_t)ordered_key(logits[(size_t)t * E + e]) << 32) | (uint32_t)(255 - e)
+                     : 0ull;
+  }
+  int sel_id[15];
+  float sel_val[15];
+#pragma unroll
+  for (int k = 0; k < 15; ++k) {
+    sel_id[k] = 0;
+    sel_val[k] = 0.f;
+    if (k < K) {
+      uint64_t best = key[0];
+#pragma unroll
+      for (int j = 1; j < 4; ++j) best = key[j] > best ? key[j] : best;
+      best = wave_max_u64(best);
+      const int e = 255 - (int)(best & 0xFFu);
+      sel_id[k] = e;
+      sel_val[k] = key_to_float((uint32_t)(best >> 32));
+      if ((e & 63) == lane) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          if (e >> 6 == j) key[j] = 0ull;   // taken: below every finite logit
+      }
+    }
+  }
+  // lane k < K takes slot k's exponent; the denominator is summed in slot order
+  float mine = 0.0f, denom = 0.0f;
+#pragma unroll
+  for (int k = 0; k < 15; ++k) {
+    if (k < K) {
+      const float p = expf(sel_val[k] - sel_val[0]);
+      denom += p;
+      if (lane == k) mine = p;
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < 15; ++k) {
+    if (k < K && lane == k) {
+      ids[(size_t)t * K1 + k] = sel_id[k];
+      w[(size_t)t * K1 + k] = __fdiv_rn(mine, denom);
+      if (lds_ids) lds_ids[t * K1 + k] = sel_id[k];
+    }
+  }
+  if (lane == K) {
+    ids[(size_t)t * K1 + K] = E;
+    w[(size_t)t * K1 + K] = shared_weight;
+    if (lds_ids) lds_ids[t * K1 + K] = E;
+  }
+}
+
+// ----------------------------------------------------------------------------- x quantisation
+__device__ __forceinline__ uint32_t encode4(float a, float b, float c, float d, float s) {
+  return e4m3_encode(__fdiv_rn(a, s)) | (e4m3_encode(__fdiv_rn(b, s)) << 8) |
+         (e4m3_encode(__fdiv_rn(c, s)) << 16) | (e4m3_encode(__fdiv_rn(d, s)) << 24);
+}
+
+__device__ __forceinline__ float4 load_bf16x4(const uint16_t* p) {
+  const uint2 v = *reinterpret_cast<const uint2*>(p);
+  return make_float4(bf16_to_f32(v.x & 0xFFFFu), bf16_to_f32(v.x >> 16), bf16_to_f32(v.y & 0xFFFFu),
+                     bf16_to_f32(v.y >> 16));
+}
+
+__device__ __forceinline__ float amax4(float4 v) {
+  return fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
+}
+
+// FP8 quantisation of token t's row of x by a group of 256 threads (tid 0..255);
+// red points at 4 LDS floats owned by the group. Per-channel: one scale for the row
+// (one pass while H <= 8192); block mode: one scale per 128 columns. Contains
+// __syncthreads(), so every thread of the workgroup must call it (valid = false
+// for groups without a token).
+template <bool kBlock>
+__device__ __forceinline__ void quant_x_token(const uint16_t* __restrict__ x, int t, bool valid, int H,
+                                              uint8_t* __restrict__ xq, float* __restrict__ sx,
+                                              int tid, float* red) {
+  const int lane = tid & 63, wv = tid >> 6;
+  const uint16_t* row = x + (size_t)t * H;
+  uint8_t* qrow = xq + (size_t)t * H;
+  if (!kBlock) {
+    constexpr int kMaxStripes = 8;
+    float4 v[kMaxStripes];
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < kMaxStripes; ++i) {
+      const int h = i * 1024 + tid * 4;
+      v[i] = (valid && h < H) ? load_bf16x4(row + h) : make_float4(0.f, 0.f, 0.f, 0.f);
+      amax = fmaxf(amax, amax4(v[i]));
+    }
+    if (valid)
+      for (int h = kMaxStripes * 1024 + tid * 4; h < H; h += 1024) amax = fmaxf(amax, amax4(load_bf16x4(row + h)));
+    amax = wave_max(amax);
+    if (lane == 0) red[wv] = amax;
+    __syncthreads();
+    const float scale = fp8_scale(fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3])));
+    if (!valid) return;
+    if (tid == 0) sx[t] = scale;
+#pragma unroll
+    for (int i = 0; i < kMaxStripes; ++i) {
+      const int h = i * 1024 + tid * 4;
+      if (h < H) *reinterpret_cast<uint32_t*>(qrow + h) = encode4(v[i].x, v[i].y, v[i].z, v[i].w, scale);
+    }
+    for (int h = kMaxStripes * 1024 + tid * 4; h < H; h += 1024) {
+      const float4 u = load_bf16x4(row + h);
+      *reinterpret_cast<uint32_t*>(qrow + h) = encode4(u.x, u.y, u.z, u.w, scale);
+    }
+  } else {
+    if (!valid) return;
+    // 128-wide groups are 32 consecutive threads; H % 128 == 0 keeps every group whole.
+    for (int h0 = 0; h0 < H; h0 += 1024) {
+      const int h = h0 + tid * 4;
+      const bool in = h < H;
+      const float4 v = in ? load_bf16x4(row + h) : make_float4(0.f, 0.f, 0.f, 0.f);
+      const float scale = fp8_scale(group_max(amax4(v), 32));
+      if (in && (tid & 31) == 0) sx[(size_t)t * (H / kGroup) + h / kGroup] = scale;
+      if (in) *reinterpret_cast<uint32_t*>(qrow + h) = encode4(v.x, v.y, v.z, v.w, scale);
+    }
+  }
+}
+
+// ----------------------------------------------------------------------------- align
+// Stable counting sort of the flat (token, slot) entries by expert. A wavefront's chunk
+// is an entry range [start, end) of at most 64 * kPer entries; lanes holding the same
+// expert find each other with 8 ballots over the bits of the expert id; a lane's rank
+// among them is the popcount of the lower lanes in that set, and the lowest lane
+// advances the chunk's running count for that expert.
+constexpr int kMaxE1 = 256;
+
+__device__ __forceinline__ uint64_t lanes_with_same_expert(int e, bool valid) {
+  uint64_t m = __ballot(valid);
+#pragma unroll
+  for (int b = 0; b < 8; ++b) {
+    const bool bit = (e >> b) & 1;
+    const uint64_t set = __ballot(valid && bit);
+    m &= bit ? set : ~set;
+  }
+  return m;
+}
+
+// entry start + 64*i + lane -> ev[i] (-1 past end); all loads issued together.
+// ids may point to global memory or to LDS.
+template <int kPer>
+__device__ __forceinline__ void load_chunk(const int32_t* ids, int start, int end, int (&ev)[kPer]) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int s = start + i * kWave + lane;
+    ev[i] = s < end ? ids[s] : -1;
+  }
+}
+
+// Count one chunk into cnt[0..E1) (LDS, zeroed by the caller).
+template <int kPer>
+__device__ __forceinline__ void count_chunk(const int (&ev)[kPer], int start, int end, int* cnt) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    if (start + i * kWave >= end) break;
+    const bool valid = ev[i] >= 0;
+    const int e = valid ? ev[i] : 0;
+    const uint64_t m = lanes_with_same_expert(e, valid);
+    if (valid && lane == __ffsll((unsigned long long)m) - 1) cnt[e] += __popcll(m);
+    __builtin_amdgcn_wave_barrier();
+  }
+}
+
+// Scatter one chunk: run[e] (LDS) starts at the chunk's first output position for e.
+template <int kPer>
+__device__ __forceinline__ void scatter_chunk(const int (&ev)[kPer], int start, int end, int* run,
+                                              int32_t* __restrict__ sorted) {
+  const int lane = threadIdx.x & 63;
+  const uint64_t lower = (1ull << lane) - 1ull;
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    if (start + i * kWave >= end) break;
+    const int s = start + i * kWave + lane;
+    const bool valid = ev[i] >= 0;
+    const int e = valid ? ev[i] : 0;
+    const uint64_t m = lanes_with_same_expert(e, valid);
+    int base = 0;
+    if (valid) base = run[e];
+    __builtin_amdgcn_wave_barrier();
+    if (valid) {
+      sorted[base + __popcll(m & lower)] = s;
+      if (lane == __ffsll((unsigned long long)m) - 1) run[e] = base + __popcll(m);
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
+}
+
+// Exclusive scan of one value per thread over the workgroup (<= 16 wavefronts);
+// wsum holds 16 ints of LDS. Returns the total.
+__device__ __forceinline__ int block_exclusive_scan(int v, int* excl, int* wsum) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  int inc = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int n = __shfl_up(inc, o, kWave);
+    if (lane >= o) inc += n;
+  }
+  if (lane == 63) wsum[wv] = inc;
+  __syncthreads();
+  int pre = 0, total = 0;
+  for (int j = 0; j < nw; ++j) {
+    if (j < wv) pre += wsum[j];
+    total += wsum[j];
+  }
+  *excl = pre + inc - v;
+  __syncthreads();
+  return total;
+}
+
+// Expert totals -> padded offsets, the outputs, and the padding/tail fills. Thread e
+// owns expert e (< E1 <= 256). off[e] (LDS) receives expert e's first row.
+__device__ __forceinline__ void finish_layout(int e, int E1, int block_m, int total_e, int sentinel,
+                                              int P_max, int* off, int* wsum,
+                                              int32_t* __restrict__ sorted,
+                                              int32_t* __restrict__ block_expert,
+                                              int32_t* __restrict__ counts,
+                                              int32_t* __restrict__ offsets,
+                                              int32_t* __restrict__ num_padded) {
+  const int padded = (e < E1) ? (total_e + block_m - 1) / block_m * block_m : 0;
+  int excl;
+  const int total = block_exclusive_scan(padded, &excl, wsum);
+  if (e < E1) {
+    off[e] = excl;
+    counts[e] = total_e;
+    offsets[e] = excl;
+    for (int r = excl + total_e; r < excl + padded; ++r) sorted[r] = sentinel;
+    for (int b = excl / block_m; b < (excl + padded) / block_m; ++b) block_expert[b] = e;
+  }
+  if (threadIdx.x == 0) {
+    offsets[E1] = total;
+    num_padded[0] = total;
+  }
+  for (int r = total + threadIdx.x; r < P_max; r += blockDim.x) sorted[r] = sentinel;
+  for (int b = total / block_m + threadIdx.x; b < P_max / block_m; b += blockDim.x) block_expert[b] = -1;
+}
+
+// Whole align of N <= 64 * kPer * (blockDim/64) entries inside one workgroup: the
+// wavefronts take consecutive ranges of the entries (in whole 64s), count them into
+// cnt[wave][E1], lay the experts out, then scatter stably. ids may be global or LDS;
+// cnt holds (blockDim/64) x kMaxE1 ints of LDS, off kMaxE1, wsum 16.
+template <int kPer>
+__device__ __forceinline__ void align_in_workgroup(const int32_t* ids, int N, int E1, int block_m,
+                                                   int P_max, int (*cnt)[kMaxE1], int* off, int* wsum,
+                                                   int32_t* __restrict__ sorted,
+                                                   int32_t* __restrict__ block_expert,
+                                                   int32_t* __restrict__ counts,
+                                                   int32_t* __restrict__ offsets,
+                                                   int32_t* __restrict__ num_padded) {
+  const int wv = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  const int per = ((N + nw * kWave - 1) / (nw * kWave)) * kWave;
+  const int start = min(wv * per, N), end = min(start + per, N);
+  int ev[kPer];
+  load_chunk<kPer>(ids, start, end, ev);
+  for (int i = threadIdx.x; i < nw * kMaxE1; i += blockDim.x) (&cnt[0][0])[i] = 0;
+  __syncthreads();
+  count_chunk<kPer>(ev, start, end, cnt[wv]);
+  __syncthreads();
+  const int e = threadIdx.x;
+  int total_e = 0;
+  if (e < E1)
+    for (int c = 0; c < nw; ++c) total_e += cnt[c][e];
+  finish_layout(e, E1, block_m, total_e, N, P_max, off, wsum, sorted, block_expert, counts, offsets,
+                num_padded);
+  __syncthreads();
+  if (e < E1) {   // per-wavefront first positions: expert offset + earlier wavefronts' counts
+    int run = off[e];
+    for (int c = 0; c < nw; ++c) {
+      const int n = cnt[c][e];
+      cnt[c][e] = run;
+      run += n;
+    }
+  }
+  __syncthreads();
+  scatter_chunk<kPer>(ev, start, end, cnt[wv], sorted);
+}
+
+}  // namespace srmoe

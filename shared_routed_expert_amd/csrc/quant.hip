@@ -5,72 +5,16 @@
 // one scale per row; block mode one per row and 128-column group. (The pages
 // run the layer in FP8 E4M3: intelliparadigm section 3.1; Optimizing GLM4-MoE
 // for production, benchmark configuration.)
-#include "common.hpp"
+#include "front_dev.hpp"
 
 namespace srmoe {
 
-__device__ __forceinline__ uint32_t encode4(float a, float b, float c, float d, float s) {
-  return e4m3_encode(__fdiv_rn(a, s)) | (e4m3_encode(__fdiv_rn(b, s)) << 8) |
-         (e4m3_encode(__fdiv_rn(c, s)) << 16) | (e4m3_encode(__fdiv_rn(d, s)) << 24);
-}
-
-__device__ __forceinline__ float4 load_bf16x4(const uint16_t* p) {
-  const uint2 v = *reinterpret_cast<const uint2*>(p);
-  return make_float4(bf16_to_f32(v.x & 0xFFFFu), bf16_to_f32(v.x >> 16), bf16_to_f32(v.y & 0xFFFFu),
-                     bf16_to_f32(v.y >> 16));
-}
-
-__device__ __forceinline__ float amax4(float4 v) {
-  return fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
-}
-
-// x [T,H] bf16 -> xq [T,H] e4m3, sx [T] or [T,H/128]. One 256-thread workgroup per
-// token; each thread takes 4 consecutive values per 1024-wide stripe.
+// x [T,H] bf16 -> xq [T,H] e4m3, sx [T] or [T,H/128]: one 256-thread workgroup per token.
 template <bool kBlock>
 __global__ void __launch_bounds__(256) quant_x_kernel(const uint16_t* __restrict__ x, int T, int H,
                                                       uint8_t* __restrict__ xq, float* __restrict__ sx) {
   __shared__ float red[4];
-  const int t = blockIdx.x;
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const uint16_t* row = x + (size_t)t * H;
-  uint8_t* qrow = xq + (size_t)t * H;
-  if (!kBlock) {
-    // one pass: H <= 8192 keeps the row in registers (8 stripes of 4 values per thread)
-    constexpr int kMaxStripes = 8;
-    float4 v[kMaxStripes];
-    float amax = 0.0f;
-#pragma unroll
-    for (int i = 0; i < kMaxStripes; ++i) {
-      const int h = i * 1024 + tid * 4;
-      v[i] = h < H ? load_bf16x4(row + h) : make_float4(0.f, 0.f, 0.f, 0.f);
-      amax = fmaxf(amax, amax4(v[i]));
-    }
-    for (int h = kMaxStripes * 1024 + tid * 4; h < H; h += 1024) amax = fmaxf(amax, amax4(load_bf16x4(row + h)));
-    amax = wave_max(amax);
-    if (lane == 0) red[wv] = amax;
-    __syncthreads();
-    const float scale = fp8_scale(fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3])));
-    if (tid == 0) sx[t] = scale;
-#pragma unroll
-    for (int i = 0; i < kMaxStripes; ++i) {
-      const int h = i * 1024 + tid * 4;
-      if (h < H) *reinterpret_cast<uint32_t*>(qrow + h) = encode4(v[i].x, v[i].y, v[i].z, v[i].w, scale);
-    }
-    for (int h = kMaxStripes * 1024 + tid * 4; h < H; h += 1024) {
-      const float4 w = load_bf16x4(row + h);
-      *reinterpret_cast<uint32_t*>(qrow + h) = encode4(w.x, w.y, w.z, w.w, scale);
-    }
-  } else {
-    // 128-wide groups are 32 consecutive threads; H % 128 == 0 keeps every group whole.
-    for (int h0 = 0; h0 < H; h0 += 1024) {
-      const int h = h0 + tid * 4;
-      const bool in = h < H;
-      const float4 v = in ? load_bf16x4(row + h) : make_float4(0.f, 0.f, 0.f, 0.f);
-      const float scale = fp8_scale(group_max(amax4(v), 32));
-      if (in && (tid & 31) == 0) sx[(size_t)t * (H / kGroup) + h / kGroup] = scale;
-      if (in) *reinterpret_cast<uint32_t*>(qrow + h) = encode4(v.x, v.y, v.z, v.w, scale);
-    }
-  }
+  quant_x_token<kBlock>(x, blockIdx.x, true, H, xq, sx, threadIdx.x, red);
 }
 
 // a [P,I] float32 -> aq [P,I] e4m3, sa [P] or [P,I/128].

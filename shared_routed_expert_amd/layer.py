@@ -99,6 +99,15 @@ class FusedMoE:
         self.combine(stream)
         return self.out
 
+    def forward_fused(self, x, logits, W: DeviceWeights, shared_weight=1.0, stream=None):
+        """The same layer through moe_layer_forward (one C call; fewer launches for small batches)."""
+        T, H, I, E1, K1, bm = self.dims()
+        L.moe_layer_forward(x, logits, W.w13, W.s13, W.w2, W.s2, self.scale_mode, T, H, I, self.E, self.K,
+                            shared_weight, bm, self.topk_ids, self.topk_w, self.sorted_slot_ids,
+                            self.block_expert, self.expert_counts, self.expert_offsets, self.num_padded,
+                            self.align_ws, self.align_ws_bytes, self.ws, self.ws_bytes, self.out, stream)
+        return self.out
+
     # views into the workspace, for inspecting the stages
     def ws_view(self, name, dtype, shape):
         off = self.offsets[name]

@@ -173,3 +173,28 @@ def test_no_cpu_fallback_in_product(L):
         if fn.endswith(".py"):
             src = open(os.path.join(pkg, fn)).read()
             assert "import oracle" not in src and "from oracle" not in src, fn
+
+
+def test_layer_forward_rejects(L):
+    def f(**kw):
+        a = dict(x=FAKE, logits=FAKE, w13=FAKE, s13=FAKE, w2=FAKE, s2=FAKE, scale_mode=0, T=64, H=5120, I=192,
+                 E=160, K=8, shared_weight=1.0, block_m=16, topk_ids=FAKE, topk_w=FAKE, sorted_slot_ids=FAKE,
+                 block_expert=FAKE, expert_counts=FAKE, expert_offsets=FAKE, num_padded=FAKE, align_ws=FAKE,
+                 align_ws_bytes=1 << 30, ffn_ws=FAKE, ffn_ws_bytes=1 << 40, out=FAKE)
+        a.update(kw)
+        return L.moe_layer_forward(**a, stream=0, check=False)
+    assert f(T=-1) == -1
+    assert f(E=0) == -1
+    assert f(K=9, E=8) == -2
+    assert f(E=256) == -2
+    assert f(H=1000) == -2
+    assert f(block_m=8) == -2
+    assert f(scale_mode=1) == -2          # I=192 is not a multiple of 128
+    for name in ("x", "logits", "w13", "s13", "w2", "s2", "topk_ids", "topk_w", "sorted_slot_ids",
+                 "block_expert", "expert_counts", "expert_offsets", "num_padded", "align_ws", "ffn_ws",
+                 "out"):
+        assert f(**{name: None}) == -1, name
+        assert f(**{name: MIS}) == -1, name
+    assert f(align_ws_bytes=16) == -3
+    assert f(ffn_ws_bytes=1024) == -3
+    assert f(T=0, x=None, out=None) == 0

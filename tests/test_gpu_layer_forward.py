@@ -1,0 +1,49 @@
+"""moe_layer_forward (one C call) against the four calls: identical bits in every output."""
+import numpy as np
+import pytest
+import torch
+
+from tests.gpu_util import DEV, note, to_dev, bf16_dev, make_layer, small_cfg
+from workloads import CONFIGS, generate
+
+pytestmark = pytest.mark.gpu
+
+
+def _outputs(layer):
+    T, H = layer.T, layer.H
+    return {
+        "topk_ids": layer.topk_ids.cpu().numpy().copy(),
+        "topk_w": layer.topk_w.cpu().numpy().view(np.int32).copy(),
+        "sorted": layer.sorted_slot_ids.cpu().numpy().copy(),
+        "block_expert": layer.block_expert.cpu().numpy().copy(),
+        "counts": layer.expert_counts.cpu().numpy().copy(),
+        "offsets": layer.expert_offsets.cpu().numpy().copy(),
+        "num_padded": layer.num_padded.cpu().numpy().copy(),
+        "xq": layer.ws_view("xq", torch.uint8, (T, H)).cpu().numpy().copy(),
+        "out": layer.out.view(torch.int16).cpu().numpy().copy(),
+    }
+
+
+@pytest.mark.parametrize("cfg,bm", [
+    (CONFIGS["tiny"], 16),
+    (small_cfg("ragged", T=77, H=384, I=96, E=12, K=3, seed=11), 32),
+    (small_cfg("block", T=50, H=384, I=256, E=6, K=2, mode="block128", seed=15), 16),
+    (small_cfg("edge_e255", T=30, H=256, I=64, E=255, K=15, seed=21), 16),
+    (small_cfg("single_wg_align", T=455, H=256, I=64, E=40, K=8, seed=22), 64),  # 4095 entries: one-workgroup align
+    (small_cfg("three_pass_align", T=600, H=256, I=64, E=40, K=8, seed=23), 64),  # 5400 entries: count/scan/scatter
+    (CONFIGS["decode"], 16),
+])
+def test_layer_forward_matches_four_calls(cfg, bm):
+    inp = generate(cfg)
+    note(f"layer_forward {cfg.name} bm={bm}")
+    x, lg = bf16_dev(inp.x_bf16), to_dev(inp.logits)
+    a, W = make_layer(inp, bm)
+    a.forward(x, lg, W, 0.75)
+    torch.cuda.synchronize()
+    ref = _outputs(a)
+    b, _ = make_layer(inp, bm)
+    b.forward_fused(x, lg, W, 0.75)
+    torch.cuda.synchronize()
+    got = _outputs(b)
+    for k in ref:
+        assert np.array_equal(ref[k], got[k]), k
