@@ -13,11 +13,11 @@ hipError_t launch_quant_x(const uint16_t*, int, int, bool, uint8_t*, float*, hip
 hipError_t launch_quant_a(const float*, int, int, bool, const int32_t*, const float*, int, uint8_t*,
                           float*, float*, hipStream_t);
 hipError_t launch_gate_up(const uint8_t*, const float*, const uint8_t*, const float*, bool,
-                          const int32_t*, const int32_t*, float*, int, int, int, int, int, int,
-                          hipStream_t);
+                          const int32_t*, const int32_t*, const int32_t*, float*, int, int, int, int,
+                          int, int, hipStream_t);
 hipError_t launch_down(const uint8_t*, const float*, const uint8_t*, const float*, bool,
-                       const int32_t*, const int32_t*, const float*, uint16_t*, int, int, int, int,
-                       int, int, hipStream_t);
+                       const int32_t*, const int32_t*, const int32_t*, const float*, uint16_t*, int,
+                       int, int, int, int, int, hipStream_t);
 hipError_t launch_combine(const uint16_t*, int, int, int, uint16_t*, hipStream_t);
 hipError_t launch_gate_up_decode(const uint8_t*, const float*, const uint8_t*, const float*, bool,
                                  const int32_t*, const int32_t*, float*, int, int, int, int, int,
@@ -196,7 +196,7 @@ int moe_ffn_gate_up(const uint8_t* w13, const float* s13, int scale_mode, int T,
                                             as_stream(stream)));
   return hip_status(launch_gate_up(reinterpret_cast<const uint8_t*>(ws + L.xq),
                                    reinterpret_cast<const float*>(ws + L.sx), w13, s13, blk,
-                                   sorted_slot_ids, block_expert,
+                                   sorted_slot_ids, block_expert, num_padded,
                                    reinterpret_cast<float*>(ws + L.a), T, H, I, E1, K1, block_m,
                                    as_stream(stream)));
 }
@@ -226,7 +226,8 @@ int moe_ffn_down(const uint8_t* w2, const float* s2, int scale_mode, int T, int 
   if (e != hipSuccess) return hip_status(e);
   return hip_status(launch_down(reinterpret_cast<const uint8_t*>(ws + L.aq),
                                 reinterpret_cast<const float*>(ws + L.sa), w2, s2, blk,
-                                sorted_slot_ids, block_expert, reinterpret_cast<const float*>(ws + L.rs),
+                                sorted_slot_ids, block_expert, num_padded,
+                                reinterpret_cast<const float*>(ws + L.rs),
                                 reinterpret_cast<uint16_t*>(ws + L.slot_out), T, H, I, E1, K1,
                                 block_m, as_stream(stream)));
 }

@@ -124,6 +124,41 @@ __device__ __forceinline__ float fp8_scale(float amax) {
   return amax > 0.0f ? __fdiv_rn(amax, kFp8Max) : 1.0f;
 }
 
+// SwiGLU gate activation silu(z) = z * sigmoid(z), in float32.
+__device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
+
+// 32 bytes (one MFMA operand's K slice for a lane) from a 16-byte aligned address.
+__device__ __forceinline__ v8i load32(const uint8_t* p) {
+  const uint4 lo = *reinterpret_cast<const uint4*>(p);
+  const uint4 hi = *reinterpret_cast<const uint4*>(p + 16);
+  v8i r;
+  r[0] = lo.x; r[1] = lo.y; r[2] = lo.z; r[3] = lo.w;
+  r[4] = hi.x; r[5] = hi.y; r[6] = hi.z; r[7] = hi.w;
+  return r;
+}
+
+// The command processor hands workgroup i of a launch to XCD i % 8, and each
+// XCD has its own L2. For a 1-D grid of at least n workgroups, map dispatch slot
+// i to a logical tile so that every XCD walks a contiguous run of the n tiles in
+// order (neighbouring tiles then share operands through one L2), every XCD gets
+// within one tile of the same count, and the slots left over get -1.
+__device__ __forceinline__ int xcd_tile(int i, int n) {
+  const int x = i & 7, j = i >> 3;
+  const int q = n >> 3, r = n & 7;
+  if (j >= q + (x < r ? 1 : 0)) return -1;
+  return x * q + (x < r ? x : r) + j;
+}
+
+// Token of sorted slot id s = t * K1 + k, i.e. floor(s / K1), as a multiply by
+// magic = ceil(2^32 / K1) (slot_div_magic). Exact for K1 <= 16 and s <= 2^24:
+// the error term s * (magic * K1 - 2^32) / (K1 * 2^32) stays below 1 / (16 K1).
+__device__ __forceinline__ uint64_t slot_div_magic(int K1) {
+  return (uint64_t)(0xFFFFFFFFu / (uint32_t)K1) + 1u;
+}
+__device__ __forceinline__ int slot_token(int s, uint64_t magic) {
+  return (int)(((uint64_t)(uint32_t)s * magic) >> 32);
+}
+
 __host__ __device__ __forceinline__ size_t sorted_capacity(int T, int K1, int E1, int block_m) {
   size_t n = (size_t)T * K1 + (size_t)E1 * (block_m - 1);
   return (n + block_m - 1) / block_m * block_m;

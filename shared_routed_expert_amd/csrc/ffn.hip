@@ -21,17 +21,6 @@
 
 namespace srmoe {
 
-__device__ __forceinline__ v8i load32(const uint8_t* p) {
-  const uint4 lo = *reinterpret_cast<const uint4*>(p);
-  const uint4 hi = *reinterpret_cast<const uint4*>(p + 16);
-  v8i r;
-  r[0] = lo.x; r[1] = lo.y; r[2] = lo.z; r[3] = lo.w;
-  r[4] = hi.x; r[5] = hi.y; r[6] = hi.z; r[7] = hi.w;
-  return r;
-}
-
-__device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
-
 // grid: (P_max / block_m, ceil(I / 64)); 4 wavefronts, each 16 intermediate columns
 // (one gate tile and the matching up tile).
 template <int MT, bool kBlock>
@@ -265,10 +254,18 @@ static hipError_t launch_gate_up_t(int block_m, dim3 grid, hipStream_t st, const
   return hipGetLastError();
 }
 
-// block_m 32..128 (block_m 16 uses launch_gate_up_decode).
+hipError_t launch_gate_up_tile(const uint8_t*, const float*, const uint8_t*, const float*, bool,
+                               const int32_t*, const int32_t*, const int32_t*, float*, int, int, int,
+                               int, int, hipStream_t);
+
+// block_m 32..128 (block_m 16 uses launch_gate_up_decode; 128 the LDS-tiled kernel).
 hipError_t launch_gate_up(const uint8_t* xq, const float* sx, const uint8_t* w13, const float* s13,
-                          bool block, const int32_t* sorted, const int32_t* block_expert, float* a,
-                          int T, int H, int I, int E1, int K1, int block_m, hipStream_t stream) {
+                          bool block, const int32_t* sorted, const int32_t* block_expert,
+                          const int32_t* num_padded, float* a, int T, int H, int I, int E1, int K1,
+                          int block_m, hipStream_t stream) {
+  if (block_m == 128)
+    return launch_gate_up_tile(xq, sx, w13, s13, block, sorted, block_expert, num_padded, a, T, H, I,
+                               E1, K1, stream);
   const int P_max = (int)sorted_capacity(T, K1, E1, block_m);
   const dim3 grid(P_max / block_m, (I + 63) / 64);
   return block ? launch_gate_up_t<true>(block_m, grid, stream, xq, sx, w13, s13, sorted, block_expert, a, T, H, I, K1)
@@ -289,10 +286,17 @@ static hipError_t launch_down_t(int block_m, dim3 grid, hipStream_t st, const ui
   return hipGetLastError();
 }
 
+hipError_t launch_down_tile(const uint8_t*, const float*, const uint8_t*, const float*, bool,
+                            const int32_t*, const int32_t*, const int32_t*, const float*, uint16_t*,
+                            int, int, int, int, int, hipStream_t);
+
 hipError_t launch_down(const uint8_t* aq, const float* sa, const uint8_t* w2, const float* s2,
                        bool block, const int32_t* sorted, const int32_t* block_expert,
-                       const float* row_scale, uint16_t* slot_out, int T, int H, int I, int E1,
-                       int K1, int block_m, hipStream_t stream) {
+                       const int32_t* num_padded, const float* row_scale, uint16_t* slot_out, int T,
+                       int H, int I, int E1, int K1, int block_m, hipStream_t stream) {
+  if (block_m == 128)
+    return launch_down_tile(aq, sa, w2, s2, block, sorted, block_expert, num_padded, row_scale,
+                            slot_out, T, H, I, E1, K1, stream);
   const int P_max = (int)sorted_capacity(T, K1, E1, block_m);
   const dim3 grid(P_max / block_m, (H + 255) / 256);
   return block ? launch_down_t<true>(block_m, grid, stream, aq, sa, w2, s2, sorted, block_expert, row_scale, slot_out, T, H, I, K1)

@@ -21,16 +21,6 @@
 
 namespace srmoe {
 
-__device__ __forceinline__ v8i ld32(const uint8_t* p) {
-  const uint4 lo = *reinterpret_cast<const uint4*>(p);
-  const uint4 hi = *reinterpret_cast<const uint4*>(p + 16);
-  v8i r;
-  r[0] = lo.x; r[1] = lo.y; r[2] = lo.z; r[3] = lo.w;
-  r[4] = hi.x; r[5] = hi.y; r[6] = hi.z; r[7] = hi.w;
-  return r;
-}
-
-__device__ __forceinline__ float silu_f(float z) { return z / (1.0f + __expf(-z)); }
 
 template <bool kBlock>
 __global__ void __launch_bounds__(256) gate_up_decode_kernel(
@@ -87,10 +77,10 @@ __global__ void __launch_bounds__(256) gate_up_decode_kernel(
 #pragma unroll
     for (int j = 0; j < kPrefetch; ++j) {
       const size_t k = (size_t)min(st + j, s1 - 1) * kGroup;
-      const v8i t = ld32(arow + k);
+      const v8i t = load32(arow + k);
       A[j] = st + j < s1 ? t : zero8;   // a repeated step contributes nothing
-      G[j] = ld32(gp + k);
-      U[j] = ld32(upp + k);
+      G[j] = load32(gp + k);
+      U[j] = load32(upp + k);
     }
     // keep every load of the batch ahead of its MFMAs (the scheduler would otherwise
     // interleave them and wait on each step in turn)
@@ -133,7 +123,7 @@ __global__ void __launch_bounds__(256) gate_up_decode_kernel(
       g = g * e_sx * e_sg;
       u = u * e_sx * e_su;
     }
-    av = silu_f(g) * u;
+    av = silu(g) * u;
   }
   a_out[(size_t)(b * 16 + erow) * I + col0 + ec] = av;
 }
