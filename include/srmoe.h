@@ -168,7 +168,8 @@ int moe_layer_forward(const uint16_t* x, const float* logits, const uint8_t* w13
 size_t moe_sorted_capacity(int T, int K1, int E1, int block_m); /* P_max, rows */
 size_t moe_align_workspace_bytes(int T, int K1, int E1);
 size_t moe_ffn_workspace_bytes(int T, int H, int I, int E1, int K1, int block_m, int scale_mode);
-/* Byte offsets inside the FFN workspace (host): out[0] slot_out [T*K1,H] bf16 (always 0),
+/* Byte offsets inside the FFN workspace (host): out[0] slot_out [T*K1,H] bf16 (always 0;
+ * followed by one scratch row of H that padding rows are written to),
  * out[1] x_q [T,H] e4m3, out[2] x scales, out[3] a [P_max,I] float32 (sorted-row order),
  * out[4] a_q [P_max,I] e4m3, out[5] a scales, out[6] per-row output scales [P_max] float32,
  * out[7] total. For inspecting the stages; returns SRMOE_OK or SRMOE_ERR_INVALID_ARG /

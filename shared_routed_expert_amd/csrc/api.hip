@@ -44,9 +44,10 @@ int hip_status(hipError_t e) {
   return SRMOE_ERR_HIP;
 }
 
-// FFN workspace: slot_out first (moe_combine reads it at offset 0), then the
-// quantised activations, the SwiGLU product in float32, its quantised copy and
-// the per-row output scale of the down GEMM.
+// FFN workspace: slot_out first (moe_combine reads it at offset 0) plus one
+// spare row that takes the down GEMM's stores for padding rows (so its stores
+// need no branch), then the quantised activations, the SwiGLU product in
+// float32, its quantised copy and the per-row output scale of the down GEMM.
 struct FfnLayout {
   size_t slot_out, xq, sx, a, aq, sa, rs, total;
 };
@@ -57,7 +58,7 @@ FfnLayout ffn_layout(int T, int H, int I, int E1, int K1, int block_m, int mode)
   const size_t gi = mode == SRMOE_SCALE_BLOCK128 ? (size_t)I / kGroup : 1;
   FfnLayout L{};
   size_t off = 0;
-  L.slot_out = off; off += al256((size_t)T * K1 * H * 2);
+  L.slot_out = off; off += al256(((size_t)T * K1 + 1) * H * 2);
   L.xq = off;       off += al256((size_t)T * H);
   L.sx = off;       off += al256((size_t)T * gh * 4);
   L.a = off;        off += al256(P * I * 4);

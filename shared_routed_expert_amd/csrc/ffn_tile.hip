@@ -380,15 +380,26 @@ __global__ void __launch_bounds__(256, 2) down_tile_kernel(
   }
 }
 
-// down for I <= 256 (at most two 128-byte K steps): no LDS and no K loop. Each
-// wavefront keeps the a_q fragments of its 64 sorted rows (all of K) in
-// registers for its whole life and sweeps kDownTiles 64-column tiles of w2[e],
-// loading each weight K slice for the next tile as soon as the MFMAs of the
-// current tile have consumed it. Workgroup = 2 row halves x 2 interleaved
-// column streams over a group of 128 * kDownTiles columns; tiles are ordered
-// row block major and walked per XCD, so the row blocks of one expert share its
-// w2 slices through L2. Output as in down_tile_kernel.
+// down for I <= 256 (at most two 128-byte K steps): no K loop. The workgroup
+// stages its block's 128 a_q rows (zero-filled from I to the K-step boundary)
+// and the w2 scales of its columns in LDS once; each wavefront then sweeps
+// kDownTiles 64-column tiles of w2[e] for one 64-row half, with the weights as
+// the MFMA A operand, loading each weight K slice for the next tile as soon as
+// the MFMAs of the current tile have consumed it. Inside a tile, row r of MFMA
+// tile n holds column (r / 4) * 16 + 4 * n + r % 4, so each lane ends with 16
+// consecutive output columns of a row. The bf16 tile then goes through a
+// wavefront-private LDS buffer so that 8 lanes write each row's 128 contiguous
+// bytes with one non-temporal store: slot_out is written once and read once by
+// the combine, and whole-line streaming stores keep it from evicting the w2
+// slices that the block's neighbours re-read from L2 (mixed with partial-line
+// stores the same reads and writes took about 1.7x as long). Workgroup = 2 row
+// halves x 2 interleaved column streams over 128 * kDownTiles columns; tiles
+// are ordered row block major and walked per XCD.
 constexpr int kDownTiles = 4;
+constexpr int kDownLD = 2 * kGroup + 16;   // LDS row stride of the a_q tile (bytes)
+constexpr int kStageLD = 128 + 16;         // LDS row stride of an output staging buffer
+
+typedef unsigned int u32x4_nt __attribute__((ext_vector_type(4)));
 
 template <bool kBlock, int KS>
 __global__ void __launch_bounds__(256, 2) down_wide_kernel(
@@ -397,7 +408,11 @@ __global__ void __launch_bounds__(256, 2) down_wide_kernel(
     const int32_t* __restrict__ block_expert, const int32_t* __restrict__ num_padded,
     const float* __restrict__ row_scale, uint16_t* __restrict__ slot_out, int T, int H, int I,
     int K1) {
-  const int ng = (H + 128 * kDownTiles - 1) / (128 * kDownTiles);
+  constexpr int kCols = 128 * kDownTiles;   // columns per workgroup
+  __shared__ __align__(16) uint8_t atile[kTBM * kDownLD];
+  __shared__ __align__(16) uint8_t stage[4][64 * kStageLD];
+  __shared__ __align__(16) float scol[kBlock ? kCols / kGroup * KS : kCols];
+  const int ng = (H + kCols - 1) / kCols;
   const int tile = xcd_tile(blockIdx.x, num_padded[0] / kTBM * ng);
   if (tile < 0) return;
   const int b = tile / ng;
@@ -408,99 +423,124 @@ __global__ void __launch_bounds__(256, 2) down_wide_kernel(
   const int r16 = lane & 15, kq = lane >> 4;
   const int wt = wv & 1, wc = wv >> 1;
   const int nct = H / 64;
-  int t = g * 2 * kDownTiles + wc;   // this wavefront's first 64-column tile
-  if (t >= nct) return;
   const int sentinel = T * K1;
-  const v8i zero8 = {0, 0, 0, 0, 0, 0, 0, 0};
-  const v4f zero4 = {0.f, 0.f, 0.f, 0.f};
+  const int c0 = g * kCols;   // first column of the workgroup
 
-  // K slices of this lane: bytes ks * 128 + kq * 32 .. +32; those past I are zero
-  uint32_t koff[KS];
-  bool kin[KS];
+  // a_q rows of the block -> LDS, bytes [I, KS * 128) of each row zeroed: 4 * KS
+  // 16-byte chunks per thread, from unconditional (clamped) loads so that the
+  // unrolled copy issues them all before the first store waits
+  {
+    constexpr int cpr = KS * kGroup / 16;   // chunks per LDS row
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
-    const int k = ks * kGroup + kq * 32;
-    kin[ks] = k < I;
-    koff[ks] = kin[ks] ? k : 0;
+    for (int i = 0; i < 4 * KS; ++i) {
+      const int c = tid + 256 * i, r = c / cpr, k = (c % cpr) * 16;
+      const uint4 v = *reinterpret_cast<const uint4*>(aq + ((size_t)b * kTBM + r) * I + (k < I ? k : 0));
+      const uint32_t msk = k < I ? 0xFFFFFFFFu : 0u;   // a per-word mask: a select of whole
+                                                       // uint4 values would go through scratch
+      *reinterpret_cast<uint4*>(&atile[r * kDownLD + k]) =
+          make_uint4(v.x & msk, v.y & msk, v.z & msk, v.w & msk);
+    }
   }
-  // a_q fragments and epilogue data of rows 64 * wt + 16 m + r16 of the block
-  v8i tf[4][KS];
-  int srow[4];
+  // w2 scales of the workgroup's columns -> LDS (per channel: kCols floats;
+  // block mode: per 128-column block and K step), clamped past H
+  if (!kBlock) {
+#pragma unroll
+    for (int i = 0; i < kCols / 256; ++i) {
+      const int c = tid + 256 * i;
+      scol[c] = s2[(size_t)e * H + min(c0 + c, H - 1)];
+    }
+  } else if (tid < kCols / kGroup * KS) {
+    const int cb = min(c0 / kGroup + tid / KS, H / kGroup - 1);
+    scol[tid] = s2[((size_t)e * (H / kGroup) + cb) * (I / kGroup) + tid % KS];
+  }
+  // this lane's rows: output scale in the MFMA layout (rows 64 wt + 16 m + r16)
+  // and slot ids in the store layout (rows 64 wt + 8 q + lane / 8)
   float rsc[4], sar[4][KS];
 #pragma unroll
   for (int m = 0; m < 4; ++m) {
     const int p = b * kTBM + 64 * wt + 16 * m + r16;
-    srow[m] = sorted[p];
     rsc[m] = row_scale[p];
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const v8i v = load32(aq + (size_t)p * I + koff[ks]);
-      tf[m][ks] = kin[ks] ? v : zero8;
-      sar[m][ks] = kBlock ? sa[(size_t)p * (I / kGroup) + ks] : 1.f;
-    }
+    for (int ks = 0; ks < KS; ++ks) sar[m][ks] = kBlock ? sa[(size_t)p * (I / kGroup) + ks] : 1.f;
   }
-  // weight fragment rows: tile row r16 of MFMA tile n is column (r16/4)*16 + 4n + r16%4
+  int srow[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q)   // padding rows go to the spare row after the T*K1 slot rows
+    srow[q] = min(sorted[b * kTBM + 64 * wt + 8 * q + (lane >> 3)], sentinel);
+  // K slices of this lane: bytes ks * 128 + kq * 32 .. +32. Weight slices past I
+  // are clamped to the row's first bytes (finite weights) and meet zeros in the
+  // a_q tile, so each such product is exactly 0.
+  uint32_t koff[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    const int k = ks * kGroup + kq * 32;
+    koff[ks] = k < I ? k : 0;
+  }
+  int t = g * 2 * kDownTiles + wc;   // this wavefront's first 64-column tile
+  const bool active = t < nct;
+  const int t0 = active ? t : 0;
+  // weight fragment rows: row r16 of MFMA tile n is column (r16/4)*16 + 4n + r16%4
   const uint8_t* wb = w2 + (size_t)e * H * I + (size_t)((r16 >> 2) * 16 + (r16 & 3)) * I;
   v8i wf[4][KS];
 #pragma unroll
   for (int n = 0; n < 4; ++n)
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const v8i v = load32(wb + (size_t)(t * 64 + 4 * n) * I + koff[ks]);
-      wf[n][ks] = kin[ks] ? v : zero8;
-    }
+    for (int ks = 0; ks < KS; ++ks) wf[n][ks] = load32(wb + (size_t)(t0 * 64 + 4 * n) * I + koff[ks]);
+  __syncthreads();   // the a_q tile and the scales are in LDS
+  if (!active) return;
+  // Drain the prologue's loads (the first MFMAs need them anyway) so that the
+  // loop entry carries no pending loads; otherwise the waits inside the loop are
+  // placed for the worse of both paths and also cover the previous tile's stores.
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0), expcnt and lgkmcnt unconstrained
 
+  const v4f zero4 = {0.f, 0.f, 0.f, 0.f};
+  const uint8_t* trow = &atile[(64 * wt + r16) * kDownLD + kq * 32];
+  uint8_t* stg = stage[wv];
   for (int j = 0; j < kDownTiles; ++j) {
     const int tn = t + 2;
     const bool more = j + 1 < kDownTiles && tn < nct;
-    const int hl = t * 64 + 16 * kq;   // this lane's first output column
-    float swc[16], swb[KS];
-    if (!kBlock) {
-#pragma unroll
-      for (int c = 0; c < 16; c += 4) {
-        const float4 v = *reinterpret_cast<const float4*>(s2 + (size_t)e * H + hl + c);
-        swc[c] = v.x; swc[c + 1] = v.y; swc[c + 2] = v.z; swc[c + 3] = v.w;
-      }
-    } else {
-#pragma unroll
-      for (int c = 0; c < 16; ++c) swc[c] = 1.f;
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-        swb[ks] = s2[((size_t)e * (H / kGroup) + (t >> 1)) * (I / kGroup) + ks];
-    }
-    v4f acc[4][4];
+    const int tl = more ? tn : t;   // tile whose weights are fetched next (re-read at the end)
+    v4f acc[4][4];   // [column tile n][row tile m]
 #pragma unroll
     for (int n = 0; n < 4; ++n)
 #pragma unroll
       for (int m = 0; m < 4; ++m) acc[n][m] = zero4;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
+      v8i tf[4];
 #pragma unroll
-      for (int n = 0; n < 4; ++n)
+      for (int m = 0; m < 4; ++m) tf[m] = load32(trow + 16 * m * kDownLD + ks * kGroup);
+      const float sb = kBlock ? scol[((t * 64 - c0) / kGroup) * KS + ks] : 1.f;
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
+      for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int n = 0; n < 4; ++n) {
           if (!kBlock) {
-            acc[n][m] = mfma_16x16x128_fp8(wf[n][ks], tf[m][ks], acc[n][m]);
+            acc[n][m] = mfma_16x16x128_fp8(wf[n][ks], tf[m], acc[n][m]);
           } else {
-            const v4f p4 = mfma_16x16x128_fp8(wf[n][ks], tf[m][ks], zero4);
-            const float sc = sar[m][ks] * swb[ks];
+            const v4f p4 = mfma_16x16x128_fp8(wf[n][ks], tf[m], zero4);
+            const float sc = sar[m][ks] * sb;
 #pragma unroll
             for (int q = 0; q < 4; ++q) acc[n][m][q] += p4[q] * sc;
           }
         }
       __builtin_amdgcn_sched_barrier(0);
-      if (more) {   // the next tile's slice ks replaces the one just consumed
+      // the next tile's slice ks replaces the one just consumed
 #pragma unroll
-        for (int n = 0; n < 4; ++n) {
-          const v8i v = load32(wb + (size_t)(tn * 64 + 4 * n) * I + koff[ks]);
-          wf[n][ks] = kin[ks] ? v : zero8;
-        }
-      }
+      for (int n = 0; n < 4; ++n) wf[n][ks] = load32(wb + (size_t)(tl * 64 + 4 * n) * I + koff[ks]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // scale, round and stage: lane (r16, kq) holds columns 16 kq .. 16 kq + 15 of
+    // rows 16 m + r16 of the wavefront's 64
+    float swc[16];
+#pragma unroll
+    for (int c = 0; c < 16; c += 4) {
+      const float4 v = kBlock ? make_float4(1.f, 1.f, 1.f, 1.f)
+                              : *reinterpret_cast<const float4*>(&scol[t * 64 - c0 + 16 * kq + c]);
+      swc[c] = v.x; swc[c + 1] = v.y; swc[c + 2] = v.z; swc[c + 3] = v.w;
     }
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
-      const int s = srow[m];
-      if (s >= sentinel) continue;
       uint32_t packed[8];
 #pragma unroll
       for (int c = 0; c < 16; c += 2) {   // column c = 4 * n + q of this lane's 16
@@ -508,9 +548,18 @@ __global__ void __launch_bounds__(256, 2) down_wide_kernel(
         const float y1 = acc[(c + 1) >> 2][m][(c + 1) & 3] * swc[c + 1] * rsc[m];
         packed[c >> 1] = (uint32_t)f32_to_bf16(y0) | ((uint32_t)f32_to_bf16(y1) << 16);
       }
-      uint4* dst = reinterpret_cast<uint4*>(slot_out + (size_t)s * H + hl);
-      dst[0] = make_uint4(packed[0], packed[1], packed[2], packed[3]);
-      dst[1] = make_uint4(packed[4], packed[5], packed[6], packed[7]);
+      uint4* sp = reinterpret_cast<uint4*>(stg + (16 * m + r16) * kStageLD + kq * 32);
+      sp[0] = make_uint4(packed[0], packed[1], packed[2], packed[3]);
+      sp[1] = make_uint4(packed[4], packed[5], packed[6], packed[7]);
+    }
+    // store: 8 lanes per row, 8 rows per instruction, each row's 128 bytes whole
+    // (a wavefront's LDS operations complete in order, so no barrier is needed)
+    const int hs = t * 64 + (lane & 7) * 8;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const uint4 v = *reinterpret_cast<const uint4*>(stg + (8 * q + (lane >> 3)) * kStageLD + (lane & 7) * 16);
+      const u32x4_nt nv = {v.x, v.y, v.z, v.w};
+      __builtin_nontemporal_store(nv, reinterpret_cast<u32x4_nt*>(slot_out + (size_t)srow[q] * H + hs));
     }
     if (!more) break;
     t = tn;
