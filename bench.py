@@ -35,7 +35,41 @@ WORKLOAD_TEXT = {
     "unsharded_block": "unsharded expert width: T=4096, H=5120, 160+1 experts, I=1536, top-8 + shared, "
                        "fp8 e4m3 weights with 128x128 block scales",
 }
-DEFAULT_BLOCK_M = {"decode": 16, "prefill": 64, "prefill16k_zipf": 128, "unsharded_block": 64, "tiny": 16}
+DEFAULT_BLOCK_M = {"decode": 16, "prefill": 128, "prefill16k_zipf": 128, "unsharded_block": 128, "tiny": 16}
+
+# HBM traffic of the dominant (gate_up) kernel per launch, from the committed rocprofv3
+# counter summary of the workload: FETCH_SIZE and WRITE_SIZE passes, each scaled by what
+# the counter reads for a plain copy of known size. The summary records a hash of the
+# kernel's source files; when the sources have changed since, the figure is null.
+TRAFFIC_PROFILES = {
+    ("decode", 16): ("profiles/gate_up_decode_T64_hbm_traffic.txt",
+                     ["shared_routed_expert_amd/csrc/ffn_decode.hip", "shared_routed_expert_amd/csrc/common.hpp"]),
+    ("prefill", 128): ("profiles/gate_up_tile_prefill_T4096_hbm_traffic.txt",
+                       ["shared_routed_expert_amd/csrc/ffn_tile.hip", "shared_routed_expert_amd/csrc/common.hpp"]),
+}
+
+
+def source_hash(files):
+    import hashlib
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profile(workload, block_m):
+    entry = TRAFFIC_PROFILES.get((workload, block_m))
+    if entry is None:
+        return None
+    path, files = entry
+    try:
+        fields = dict(line.split(":", 1) for line in open(os.path.join(ROOT, path)) if ":" in line)
+    except OSError:
+        return None
+    if fields.get("source_sha256", "").strip() != source_hash(files):
+        return None
+    return int(fields["traffic_bytes_per_launch"])
 
 
 def log(msg):
@@ -211,7 +245,7 @@ def main():
                    "weight_sets_cycled": len(weights), "active_experts": active, "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "kernel": "gate_up", "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": None, "alg_bytes_per_launch": gate_up_bytes,
+                     "traffic": traffic_from_profile(args.workload, bm), "alg_bytes_per_launch": gate_up_bytes,
                      "avg_launch_us": round(stage_us["gate_up"], 2)},
         "layer": {"alg_bytes": layer_bytes, "alg_GBps": round(layer_bytes / step_s / 1e9, 1),
                   "hbm_frac": round(layer_bytes / step_s / 1e9 / HBM_PEAK_GBS, 4),
