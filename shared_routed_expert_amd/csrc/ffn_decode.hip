@@ -21,6 +21,7 @@
 
 namespace srmoe {
 
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 template <bool kBlock>
 __global__ void __launch_bounds__(256) gate_up_decode_kernel(
@@ -29,7 +30,10 @@ __global__ void __launch_bounds__(256) gate_up_decode_kernel(
     const int32_t* __restrict__ block_expert, float* __restrict__ a_out, int T, int H, int I,
     int K1) {
   constexpr int kPrefetch = 5;
+  constexpr int kRS = kGroup + 16;   // LDS row stride of a staged K step (conflict-free fragment reads)
   __shared__ float red[4][2][16][17];
+  // per wavefront, one K step of its 48 rows: x rows 0..15, gate rows 16..31, up rows 32..47
+  __shared__ __align__(16) uint8_t stage[4][48 * kRS];
   const int b = blockIdx.x;
   const int e = block_expert[b];   // -1 past the used rows
   const int erow = threadIdx.x >> 4, ec = threadIdx.x & 15;   // epilogue element of this thread
@@ -43,13 +47,27 @@ __global__ void __launch_bounds__(256) gate_up_decode_kernel(
   const int nsteps = H / kGroup;
   const int s0 = wv * nsteps / 4, s1 = (wv + 1) * nsteps / 4;
 
-  // No load below is predicated per lane, so the compiler's memory waits stay exact:
-  // padding rows read token 0 (their outputs are discarded) and the unused slots of
-  // the last prefetch batch re-read the wavefront's last step.
-  const int s_in = sorted[b * 16 + r16];
-  const uint8_t* arow = xq + (size_t)(s_in < sentinel ? s_in / K1 : 0) * H + kq * 32;
-  const uint8_t* gp = w13 + ((size_t)e * 2 * I + col0 + r16) * H + kq * 32;
-  const uint8_t* upp = gp + (size_t)I * H;
+  // Loads are whole 128-byte lines: load instruction i of a K step covers rows
+  // 8 i .. 8 i + 7 of the 48 (lane l: row 8 i + l / 8, bytes 16 (l % 8) .. +15),
+  // 21% faster to stream than loading the MFMA fragments directly (16 rows x 64
+  // bytes per instruction). Each step then passes through the wavefront's LDS
+  // buffer into the fragment layout. No load is predicated per lane, so the
+  // compiler's memory waits stay exact: padding rows read token 0 (their outputs
+  // are discarded) and the unused slots of the last batch re-read the last step.
+  const uint8_t* rowp[6];
+  const int r8 = lane >> 3;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {   // x rows of the block's tokens
+    const int s_in = sorted[b * 16 + 8 * i + r8];
+    const uint32_t t = (uint32_t)s_in / (uint32_t)K1;
+    rowp[i] = xq + (size_t)(s_in < sentinel ? t : 0u) * H + (lane & 7) * 16;
+  }
+  const uint8_t* wrow = w13 + ((size_t)e * 2 * I + col0 + r8) * H + (lane & 7) * 16;
+  rowp[2] = wrow;                              // gate rows col0 .. col0 + 7
+  rowp[3] = wrow + (size_t)8 * H;              // gate rows col0 + 8 .. + 15
+  rowp[4] = wrow + (size_t)I * H;              // up rows
+  rowp[5] = wrow + (size_t)(I + 8) * H;
+  uint8_t* stg = stage[wv];
   int otok[4] = {0, 0, 0, 0};
   bool oval[4] = {false, false, false, false};
   if (kBlock) {
@@ -71,29 +89,40 @@ __global__ void __launch_bounds__(256) gate_up_decode_kernel(
     e_sx = sx[s_epi < sentinel ? s_epi / K1 : 0];
   }
 
-  const v8i zero8 = {0, 0, 0, 0, 0, 0, 0, 0};
   for (int st = s0; st < s1; st += kPrefetch) {
-    v8i A[kPrefetch], G[kPrefetch], U[kPrefetch];
+    u32x4 L[kPrefetch][6];
 #pragma unroll
     for (int j = 0; j < kPrefetch; ++j) {
       const size_t k = (size_t)min(st + j, s1 - 1) * kGroup;
-      const v8i t = load32(arow + k);
-      A[j] = st + j < s1 ? t : zero8;   // a repeated step contributes nothing
-      G[j] = load32(gp + k);
-      U[j] = load32(upp + k);
+#pragma unroll
+      for (int i = 0; i < 6; ++i) L[j][i] = *reinterpret_cast<const u32x4*>(rowp[i] + k);
     }
     // keep every load of the batch ahead of its MFMAs (the scheduler would otherwise
     // interleave them and wait on each step in turn)
     __builtin_amdgcn_sched_barrier(0);
+    const v8i zero8 = {0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
     for (int j = 0; j < kPrefetch; ++j) {
+      // one K step through LDS: rows in, fragments out (a wavefront's LDS
+      // operations complete in order, so the buffer is reused without a barrier)
+#pragma unroll
+      for (int i = 0; i < 6; ++i) {
+        // opaque to the optimiser: a plain load-then-store pair is merged into one
+        // global-to-LDS copy at the store, which would move the load behind the barrier
+        asm volatile("" : "+v"(L[j][i]));
+        *reinterpret_cast<u32x4*>(stg + (8 * i + r8) * kRS + (lane & 7) * 16) = L[j][i];
+      }
+      const v8i At = load32(stg + r16 * kRS + kq * 32);
+      const v8i A = st + j < s1 ? At : zero8;   // a repeated step contributes nothing
+      const v8i G = load32(stg + (16 + r16) * kRS + kq * 32);
+      const v8i U = load32(stg + (32 + r16) * kRS + kq * 32);
       if (!kBlock) {
-        accg = mfma_16x16x128_fp8(A[j], G[j], accg);
-        accu = mfma_16x16x128_fp8(A[j], U[j], accu);
+        accg = mfma_16x16x128_fp8(A, G, accg);
+        accu = mfma_16x16x128_fp8(A, U, accu);
       } else if (st + j < s1) {
         const int kb = st + j;
-        const v4f tg = mfma_16x16x128_fp8(A[j], G[j], zero4);
-        const v4f tu = mfma_16x16x128_fp8(A[j], U[j], zero4);
+        const v4f tg = mfma_16x16x128_fp8(A, G, zero4);
+        const v4f tu = mfma_16x16x128_fp8(A, U, zero4);
         const float swg = s13[sg_base + kb], swu = s13[su_base + kb];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
