@@ -290,6 +290,11 @@ hipError_t launch_down_tile(const uint8_t*, const float*, const uint8_t*, const 
                             const int32_t*, const int32_t*, const int32_t*, const float*, uint16_t*,
                             int, int, int, int, int, hipStream_t);
 
+bool down_decode_supported(int I);
+hipError_t launch_down_decode(const uint8_t*, const float*, const uint8_t*, const float*, bool,
+                              const int32_t*, const int32_t*, const float*, uint16_t*, int, int,
+                              int, int, int, hipStream_t);
+
 hipError_t launch_down(const uint8_t* aq, const float* sa, const uint8_t* w2, const float* s2,
                        bool block, const int32_t* sorted, const int32_t* block_expert,
                        const int32_t* num_padded, const float* row_scale, uint16_t* slot_out, int T,
@@ -297,6 +302,9 @@ hipError_t launch_down(const uint8_t* aq, const float* sa, const uint8_t* w2, co
   if (block_m == 128)
     return launch_down_tile(aq, sa, w2, s2, block, sorted, block_expert, num_padded, row_scale,
                             slot_out, T, H, I, E1, K1, stream);
+  if (block_m == 16 && down_decode_supported(I))
+    return launch_down_decode(aq, sa, w2, s2, block, sorted, block_expert, row_scale, slot_out, T,
+                              H, I, E1, K1, stream);
   const int P_max = (int)sorted_capacity(T, K1, E1, block_m);
   const dim3 grid(P_max / block_m, (H + 255) / 256);
   return block ? launch_down_t<true>(block_m, grid, stream, aq, sa, w2, s2, sorted, block_expert, row_scale, slot_out, T, H, I, K1)

@@ -157,6 +157,136 @@ __global__ void __launch_bounds__(256) gate_up_decode_kernel(
   a_out[(size_t)(b * 16 + erow) * I + col0 + ec] = av;
 }
 
+// down for 16-row blocks and I <= 256: one 256-thread workgroup per (block, 256
+// output columns) like the generic kernel (row tile of 16, the weights as the
+// MFMA A operand, lane (r16, kq) ending with 16 consecutive columns of row r16),
+// but each wavefront's 64 weight rows -- 64 * I contiguous bytes -- are loaded as
+// whole 1 KB runs and passed through a per-wavefront LDS buffer into the
+// fragment layout. Column c of the wavefront's 64 goes to LDS row
+// 16 ((c / 4) % 4) + 4 (c / 16) + c % 4, so MFMA tile n reads rows 16 n .. 16 n + 15
+// in lane order; with a row stride of I + 16 bytes those reads are bank-conflict
+// free. Both K steps run, the second (or its tail) with a zeroed a_q operand and
+// clamped weight offsets, as in the generic kernel.
+template <bool kBlock, int NI>   // NI = I / 16: 1 KB load runs per wavefront
+__global__ void __launch_bounds__(256) down_decode_kernel(
+    const uint8_t* __restrict__ aq, const float* __restrict__ sa, const uint8_t* __restrict__ w2,
+    const float* __restrict__ s2, const int32_t* __restrict__ sorted,
+    const int32_t* __restrict__ block_expert, const float* __restrict__ row_scale,
+    uint16_t* __restrict__ slot_out, int T, int H, int K1) {
+  constexpr int I = NI * 16;
+  constexpr int kRS = I + 16;
+  __shared__ __align__(16) uint8_t stage[4][64 * kRS];
+  const int b = blockIdx.x;
+  const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int r16 = lane & 15, kq = lane >> 4;
+  const int h0 = blockIdx.y * 256 + wv * 64;
+  const int e = block_expert[b];   // -1 past the used rows
+  const int srow = sorted[b * 16 + r16];
+  const float rsc = row_scale[b * 16 + r16];
+  if (e < 0 || h0 >= H) return;
+  const int sentinel = T * K1;
+  const v8i zero8 = {0, 0, 0, 0, 0, 0, 0, 0};
+  const v4f zero4 = {0.f, 0.f, 0.f, 0.f};
+
+  // the wavefront's 64 rows of w2[e]: 64 * I contiguous bytes, 1 KB per load
+  const uint8_t* wsrc = w2 + ((size_t)e * H + h0) * I + lane * 16;
+  u32x4 L[NI];
+#pragma unroll
+  for (int i = 0; i < NI; ++i) L[i] = *reinterpret_cast<const u32x4*>(wsrc + i * 1024);
+  uint32_t kc[2];
+  v8i av[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int koff = u * kGroup + kq * 32;
+    const bool in = koff < I;
+    kc[u] = in ? koff : I - 32;
+    const v8i t = load32(aq + (size_t)(b * 16 + r16) * I + kc[u]);
+    av[u] = in ? t : zero8;
+  }
+  float sw[16];
+#pragma unroll
+  for (int c = 0; c < 16; c += 4) {
+    const float4 v = kBlock ? make_float4(1.f, 1.f, 1.f, 1.f)
+                            : *reinterpret_cast<const float4*>(s2 + (size_t)e * H + h0 + kq * 16 + c);
+    sw[c] = v.x; sw[c + 1] = v.y; sw[c + 2] = v.z; sw[c + 3] = v.w;
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  uint8_t* stg = stage[wv];
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int o = i * 1024 + lane * 16;
+    const int c = o / I, byte = o - c * I;
+    const int lr = 16 * ((c >> 2) & 3) + 4 * (c >> 4) + (c & 3);
+    asm volatile("" : "+v"(L[i]));   // keeps the load ahead of the barrier (see gate_up)
+    *reinterpret_cast<u32x4*>(stg + lr * kRS + byte) = L[i];
+  }
+  v4f acc[4] = {zero4, zero4, zero4, zero4};
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    v8i bw[4];
+#pragma unroll
+    for (int n = 0; n < 4; ++n) bw[n] = load32(stg + (16 * n + r16) * kRS + kc[u]);
+    if (!kBlock) {
+#pragma unroll
+      for (int n = 0; n < 4; ++n) acc[n] = mfma_16x16x128_fp8(bw[n], av[u], acc[n]);
+    } else if (u * kGroup < I) {
+      const int kb = u;
+      // a wavefront's 64 columns lie in one 128-column block of w2's scales
+      const float swb = s2[((size_t)e * (H / kGroup) + h0 / kGroup) * (I / kGroup) + kb];
+      const float sr = sa[(size_t)(b * 16 + r16) * (I / kGroup) + kb] * swb;
+#pragma unroll
+      for (int n = 0; n < 4; ++n) {
+        const v4f t = mfma_16x16x128_fp8(bw[n], av[u], zero4);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[n][j] += t[j] * sr;
+      }
+    }
+  }
+  // the MFMAs read their scale operands across the whole wavefront: keep them ahead of the
+  // per-row exit below, under a full exec mask
+#pragma unroll
+  for (int n = 0; n < 4; ++n) asm volatile("" : "+v"(acc[n]));
+  if (srow >= sentinel) return;
+  uint32_t packed[8];
+#pragma unroll
+  for (int c = 0; c < 16; c += 2) {   // column c = 4 * n + j of this lane's 16
+    const float y0 = acc[c >> 2][c & 3] * sw[c] * rsc;
+    const float y1 = acc[(c + 1) >> 2][(c + 1) & 3] * sw[c + 1] * rsc;
+    packed[c >> 1] = (uint32_t)f32_to_bf16(y0) | ((uint32_t)f32_to_bf16(y1) << 16);
+  }
+  uint4* dst = reinterpret_cast<uint4*>(slot_out + (size_t)srow * H + h0 + kq * 16);
+  dst[0] = make_uint4(packed[0], packed[1], packed[2], packed[3]);
+  dst[1] = make_uint4(packed[4], packed[5], packed[6], packed[7]);
+}
+
+bool down_decode_supported(int I) { return I >= 32 && I <= 2 * kGroup && I % 32 == 0; }
+
+hipError_t launch_down_decode(const uint8_t* aq, const float* sa, const uint8_t* w2,
+                              const float* s2, bool block, const int32_t* sorted,
+                              const int32_t* block_expert, const float* row_scale,
+                              uint16_t* slot_out, int T, int H, int I, int E1, int K1,
+                              hipStream_t stream) {
+  const int P_max = (int)sorted_capacity(T, K1, E1, 16);
+  const dim3 grid(P_max / 16, (H + 255) / 256), blk(256);
+#define SRMOE_DD(B, N)                                                                            \
+  hipLaunchKernelGGL((down_decode_kernel<B, N>), grid, blk, 0, stream, aq, sa, w2, s2, sorted,    \
+                     block_expert, row_scale, slot_out, T, H, K1)
+#define SRMOE_DD2(N) if (block) SRMOE_DD(true, N); else SRMOE_DD(false, N); break;
+  switch (I / 16) {
+    case 2: SRMOE_DD2(2)
+    case 4: SRMOE_DD2(4)
+    case 6: SRMOE_DD2(6)
+    case 8: SRMOE_DD2(8)
+    case 10: SRMOE_DD2(10)
+    case 12: SRMOE_DD2(12)
+    case 14: SRMOE_DD2(14)
+    default: SRMOE_DD2(16)
+  }
+#undef SRMOE_DD2
+#undef SRMOE_DD
+  return hipGetLastError();
+}
+
 hipError_t launch_gate_up_decode(const uint8_t* xq, const float* sx, const uint8_t* w13,
                                  const float* s13, bool block, const int32_t* sorted,
                                  const int32_t* block_expert, float* a, int T, int H, int I, int E1,
