@@ -37,13 +37,15 @@ WORKLOAD_TEXT = {
 }
 DEFAULT_BLOCK_M = {"decode": 16, "prefill": 128, "prefill16k_zipf": 128, "unsharded_block": 128, "tiny": 16}
 
-# HBM traffic of the dominant (gate_up) kernel per launch, from the committed rocprofv3
-# counter summary of the workload: FETCH_SIZE and WRITE_SIZE passes, each scaled by what
-# the counter reads for a plain copy of known size. The summary records a hash of the
-# kernel's source files; when the sources have changed since, the figure is null.
+# HBM traffic of the dominant kernel per launch (the one-kernel expert FFN for decode, the
+# gate/up GEMM for prefill), from the committed rocprofv3 counter summary of the workload:
+# FETCH_SIZE and WRITE_SIZE passes, each scaled by what the counter reads for a plain copy
+# of known size. The summary records a hash of the kernel's source files; when the sources
+# have changed since, the figure is null.
 TRAFFIC_PROFILES = {
-    ("decode", 16): ("profiles/gate_up_decode_T64_hbm_traffic.txt",
-                     ["shared_routed_expert_amd/csrc/ffn_decode.hip", "shared_routed_expert_amd/csrc/common.hpp"]),
+    ("decode", 16): ("profiles/expert_ffn_decode_T64_hbm_traffic.txt",
+                     ["shared_routed_expert_amd/csrc/ffn_expert_decode.hip",
+                      "shared_routed_expert_amd/csrc/common.hpp"]),
     ("prefill", 128): ("profiles/gate_up_tile_prefill_T4096_hbm_traffic.txt",
                        ["shared_routed_expert_amd/csrc/ffn_tile.hip", "shared_routed_expert_amd/csrc/common.hpp"]),
 }
@@ -193,7 +195,8 @@ def main():
 
     # Timed region 2: the same steps with HIP events between the stages (same stream),
     # giving each stage's average duration, the dominant kernel's included.
-    names = ["route", "align", "quant_x", "gate_up", "down", "combine"]
+    ffn_names = layer.ffn_stage_names()
+    names = ["route", "align"] + ffn_names + ["combine"]
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     for i in range(args.steps):
@@ -204,10 +207,10 @@ def main():
         e[1].record(stream)
         layer.align(stream)
         e[2].record(stream)
-        marks = iter(e[3:6])
+        marks = iter(e[3:3 + len(ffn_names)])
         layer.ffn_stages(x, W, stream, between=lambda _n: next(marks).record(stream))
         layer.combine(stream)
-        e[6].record(stream)
+        e[len(names)].record(stream)
     torch.cuda.synchronize()
     stage_us = {n: 1e3 * statistics.mean(evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(args.steps))
                 for j, n in enumerate(names)}
@@ -218,11 +221,18 @@ def main():
     blk = cfg.scale_mode == "block128"
     s13_bytes = (2 * I // 128) * (H // 128) * 4 if blk else 2 * I * 4
     s2_bytes = (H // 128) * (I // 128) * 4 if blk else H * 4
-    # Algorithmic bytes of the gate_up kernel: each activated expert's W13 (2*I*H fp8) and its
-    # scales read once, plus the quantised activations x_q (T*H fp8) read once.
-    gate_up_bytes = active * (2 * I * H + s13_bytes) + T * H
-    gate_up_s = stage_us["gate_up"] * 1e-6
-    achieved = gate_up_bytes / gate_up_s / 1e9
+    if "experts" in stage_us:
+        # Algorithmic bytes of the one-kernel expert FFN: each activated expert's W13 (2*I*H fp8),
+        # W2 (I*H fp8) and their scales read once, x_q (T*H fp8) read once, and the weighted
+        # bf16 slot rows (T*K1*H*2) written once.
+        dom = "experts"
+        dom_bytes = active * (3 * I * H + s13_bytes + s2_bytes) + T * H + T * K1 * H * 2
+    else:
+        # Algorithmic bytes of the gate_up kernel: each activated expert's W13 (2*I*H fp8) and
+        # its scales read once, plus the quantised activations x_q (T*H fp8) read once.
+        dom = "gate_up"
+        dom_bytes = active * (2 * I * H + s13_bytes) + T * H
+    achieved = dom_bytes / (stage_us[dom] * 1e-6) / 1e9
     layer_bytes = active * (3 * I * H + s13_bytes + s2_bytes) + T * H * 2 * 2 + T * cfg.E * 4 + T * K1 * 8
     flops = T * K1 * 6 * H * I
     step_s = ms_per_step * 1e-3
@@ -243,10 +253,10 @@ def main():
         "config": {"workload": WORKLOAD_TEXT[args.workload], "T": T, "H": H, "I": I, "routed_experts": cfg.E,
                    "shared_experts": 1, "top_k": cfg.K, "slots": K1, "block_m": bm,
                    "weight_sets_cycled": len(weights), "active_experts": active, "parallelism": "single GPU"},
-        "roofline": {"bound": "hbm", "kernel": "gate_up", "achieved": round(achieved, 1),
+        "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": traffic_from_profile(args.workload, bm), "alg_bytes_per_launch": gate_up_bytes,
-                     "avg_launch_us": round(stage_us["gate_up"], 2)},
+                     "traffic": traffic_from_profile(args.workload, bm), "alg_bytes_per_launch": dom_bytes,
+                     "avg_launch_us": round(stage_us[dom], 2)},
         "layer": {"alg_bytes": layer_bytes, "alg_GBps": round(layer_bytes / step_s / 1e9, 1),
                   "hbm_frac": round(layer_bytes / step_s / 1e9 / HBM_PEAK_GBS, 4),
                   "alg_TFLOPs": round(flops / step_s / 1e12, 2),

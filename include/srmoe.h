@@ -126,10 +126,25 @@ int moe_fused_ffn(const uint16_t* x, const uint8_t* w13, const float* s13, const
                   const int32_t* num_padded, const float* topk_w, void* workspace,
                   size_t ws_bytes, void* stream);
 
-/* The three stages of moe_fused_ffn, callable one at a time (same arguments,
- * same workspace; call them in this order). moe_fused_ffn == all three. */
+/* The stages of moe_fused_ffn, callable one at a time (same arguments, same
+ * workspace). moe_fused_ffn == moe_ffn_quant_x then moe_ffn_experts.
+ *
+ * moe_ffn_experts: gate/up, a = silu(g)*u, a's FP8 quantisation and down, from the
+ * x_q that moe_ffn_quant_x left in the workspace; leaves slot_out (and the float32
+ * a) in the workspace. For 16-row blocks (block_m == 16) with I a multiple of 64 in
+ * 64..256 and H <= 5120 this is one kernel per layer (moe_ffn_experts_one_kernel
+ * says whether it is, returning 1 or 0); otherwise it is moe_ffn_gate_up followed by
+ * moe_ffn_down, which can also be called on their own (in that order). Both routes
+ * compute the same quantities; their float32 sums may round differently.
+ * Errors as moe_fused_ffn; nothing is launched when a check fails. */
 int moe_ffn_quant_x(const uint16_t* x, int scale_mode, int T, int H, int I, int E1, int K1,
                     int block_m, void* workspace, size_t ws_bytes, void* stream);
+int moe_ffn_experts(const uint8_t* w13, const float* s13, const uint8_t* w2, const float* s2,
+                    int scale_mode, int T, int H, int I, int E1, int K1, int block_m,
+                    const int32_t* sorted_slot_ids, const int32_t* block_expert,
+                    const int32_t* num_padded, const float* topk_w, void* workspace, size_t ws_bytes,
+                    void* stream);
+int moe_ffn_experts_one_kernel(int H, int I, int block_m);
 int moe_ffn_gate_up(const uint8_t* w13, const float* s13, int scale_mode, int T, int H, int I,
                     int E1, int K1, int block_m, const int32_t* sorted_slot_ids,
                     const int32_t* block_expert, const int32_t* num_padded, void* workspace,

@@ -38,6 +38,8 @@ def _load():
         "moe_ffn_quant_x": ([P, I, I, I, I, I, I, I, P, Z, P], I),
         "moe_ffn_gate_up": ([P, P, I, I, I, I, I, I, I, P, P, P, P, Z, P], I),
         "moe_ffn_down": ([P, P, I, I, I, I, I, I, I, P, P, P, P, P, Z, P], I),
+        "moe_ffn_experts": ([P, P, P, P, I, I, I, I, I, I, I, P, P, P, P, P, Z, P], I),
+        "moe_ffn_experts_one_kernel": ([I, I, I], I),
         "moe_combine": ([I, I, I, P, Z, P, P], I),
         "moe_layer_forward": ([P, P, P, P, P, P, I, I, I, I, I, I, F, I, P, P, P, P, P, P, P, P, Z, P, Z, P, P], I),
         "moe_sorted_capacity": ([I, I, I, I], Z),
@@ -57,7 +59,8 @@ def _load():
 lib = _load()
 
 EXPORTED = ("moe_route_topk_plus_shared", "moe_align_by_expert", "moe_fused_ffn", "moe_ffn_quant_x",
-            "moe_ffn_gate_up", "moe_ffn_down", "moe_combine", "moe_layer_forward", "moe_sorted_capacity",
+            "moe_ffn_gate_up", "moe_ffn_down", "moe_ffn_experts", "moe_ffn_experts_one_kernel",
+            "moe_combine", "moe_layer_forward", "moe_sorted_capacity",
             "moe_align_workspace_bytes", "moe_ffn_workspace_bytes", "moe_ffn_workspace_offsets",
             "srmoe_status_string",
             "srmoe_last_hip_error")
@@ -149,6 +152,18 @@ def moe_ffn_down(w2, s2, scale_mode, T, H, I, E1, K1, block_m, sorted_slot_ids, 
                           _ptr(sorted_slot_ids), _ptr(block_expert), _ptr(num_padded), _ptr(topk_w),
                           _ptr(workspace), ws_bytes, _stream(stream))
     return _check("moe_ffn_down", st) if check else st
+
+
+def moe_ffn_experts(w13, s13, w2, s2, scale_mode, T, H, I, E1, K1, block_m, sorted_slot_ids, block_expert,
+                    num_padded, topk_w, workspace, ws_bytes, stream=None, check=True):
+    st = lib.moe_ffn_experts(_ptr(w13), _ptr(s13), _ptr(w2), _ptr(s2), scale_mode, T, H, I, E1, K1, block_m,
+                             _ptr(sorted_slot_ids), _ptr(block_expert), _ptr(num_padded), _ptr(topk_w),
+                             _ptr(workspace), ws_bytes, _stream(stream))
+    return _check("moe_ffn_experts", st) if check else st
+
+
+def moe_ffn_experts_one_kernel(H, I, block_m):
+    return bool(lib.moe_ffn_experts_one_kernel(H, I, block_m))
 
 
 def moe_combine(T, K1, H, workspace, ws_bytes, out, stream=None, check=True):

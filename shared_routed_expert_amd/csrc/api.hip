@@ -24,6 +24,11 @@ hipError_t launch_gate_up_decode(const uint8_t*, const float*, const uint8_t*, c
                                  hipStream_t);
 hipError_t launch_layer_front(const float*, int, int, int, float, int32_t*, float*, const uint16_t*,
                               int, bool, uint8_t*, float*, hipStream_t);
+bool expert_ffn_decode_supported(int H, int I);
+hipError_t launch_expert_ffn_decode(const uint8_t*, const float*, const uint8_t*, const float*,
+                                    const uint8_t*, const float*, bool, const int32_t*, const int32_t*,
+                                    const float*, float*, uint16_t*, int, int, int, int, int,
+                                    hipStream_t);
 }  // namespace srmoe
 
 using namespace srmoe;
@@ -233,6 +238,42 @@ int moe_ffn_down(const uint8_t* w2, const float* s2, int scale_mode, int T, int 
                                 block_m, as_stream(stream)));
 }
 
+int moe_ffn_experts_one_kernel(int H, int I, int block_m) {
+  return block_m == 16 && expert_ffn_decode_supported(H, I) ? 1 : 0;
+}
+
+int moe_ffn_experts(const uint8_t* w13, const float* s13, const uint8_t* w2, const float* s2,
+                    int scale_mode, int T, int H, int I, int E1, int K1, int block_m,
+                    const int32_t* sorted_slot_ids, const int32_t* block_expert,
+                    const int32_t* num_padded, const float* topk_w, void* workspace, size_t ws_bytes,
+                    void* stream) {
+  int st = check_ffn_dims(scale_mode, T, H, I, E1, K1, block_m);
+  if (st != SRMOE_OK) return st;
+  if (T == 0) return SRMOE_OK;
+  if (!w13 || !s13 || !w2 || !s2 || !sorted_slot_ids || !block_expert || !num_padded || !topk_w ||
+      !workspace)
+    return SRMOE_ERR_INVALID_ARG;
+  if (!aligned16(w13) || !aligned16(s13) || !aligned16(w2) || !aligned16(s2) ||
+      !aligned16(sorted_slot_ids) || !aligned16(block_expert) || !aligned16(num_padded) ||
+      !aligned16(topk_w) || !aligned16(workspace))
+    return SRMOE_ERR_INVALID_ARG;
+  const FfnLayout L = ffn_layout(T, H, I, E1, K1, block_m, scale_mode);
+  if (ws_bytes < L.total) return SRMOE_ERR_WORKSPACE;
+  if (!moe_ffn_experts_one_kernel(H, I, block_m)) {
+    st = moe_ffn_gate_up(w13, s13, scale_mode, T, H, I, E1, K1, block_m, sorted_slot_ids,
+                         block_expert, num_padded, workspace, ws_bytes, stream);
+    if (st != SRMOE_OK) return st;
+    return moe_ffn_down(w2, s2, scale_mode, T, H, I, E1, K1, block_m, sorted_slot_ids, block_expert,
+                        num_padded, topk_w, workspace, ws_bytes, stream);
+  }
+  char* ws = static_cast<char*>(workspace);
+  return hip_status(launch_expert_ffn_decode(
+      reinterpret_cast<const uint8_t*>(ws + L.xq), reinterpret_cast<const float*>(ws + L.sx), w13, s13,
+      w2, s2, scale_mode == SRMOE_SCALE_BLOCK128, sorted_slot_ids, block_expert, topk_w,
+      reinterpret_cast<float*>(ws + L.a), reinterpret_cast<uint16_t*>(ws + L.slot_out), T, H, I, E1,
+      K1, as_stream(stream)));
+}
+
 int moe_fused_ffn(const uint16_t* x, const uint8_t* w13, const float* s13, const uint8_t* w2,
                   const float* s2, int scale_mode, int T, int H, int I, int E1, int K1,
                   int block_m, const int32_t* sorted_slot_ids, const int32_t* block_expert,
@@ -252,11 +293,8 @@ int moe_fused_ffn(const uint16_t* x, const uint8_t* w13, const float* s13, const
   if (ws_bytes < ffn_layout(T, H, I, E1, K1, block_m, scale_mode).total) return SRMOE_ERR_WORKSPACE;
   st = moe_ffn_quant_x(x, scale_mode, T, H, I, E1, K1, block_m, workspace, ws_bytes, stream);
   if (st != SRMOE_OK) return st;
-  st = moe_ffn_gate_up(w13, s13, scale_mode, T, H, I, E1, K1, block_m, sorted_slot_ids, block_expert,
-                       num_padded, workspace, ws_bytes, stream);
-  if (st != SRMOE_OK) return st;
-  return moe_ffn_down(w2, s2, scale_mode, T, H, I, E1, K1, block_m, sorted_slot_ids, block_expert,
-                      num_padded, topk_w, workspace, ws_bytes, stream);
+  return moe_ffn_experts(w13, s13, w2, s2, scale_mode, T, H, I, E1, K1, block_m, sorted_slot_ids,
+                         block_expert, num_padded, topk_w, workspace, ws_bytes, stream);
 }
 
 int moe_layer_forward(const uint16_t* x, const float* logits, const uint8_t* w13, const float* s13,
@@ -290,11 +328,8 @@ int moe_layer_forward(const uint16_t* x, const float* logits, const uint8_t* w13
   st = moe_align_by_expert(topk_ids, T, K1, E1, block_m, sorted_slot_ids, block_expert, expert_counts,
                            expert_offsets, num_padded, align_ws, align_ws_bytes, stream);
   if (st != SRMOE_OK) return st;
-  st = moe_ffn_gate_up(w13, s13, scale_mode, T, H, I, E1, K1, block_m, sorted_slot_ids, block_expert,
-                       num_padded, ffn_ws, ffn_ws_bytes, stream);
-  if (st != SRMOE_OK) return st;
-  st = moe_ffn_down(w2, s2, scale_mode, T, H, I, E1, K1, block_m, sorted_slot_ids, block_expert,
-                    num_padded, topk_w, ffn_ws, ffn_ws_bytes, stream);
+  st = moe_ffn_experts(w13, s13, w2, s2, scale_mode, T, H, I, E1, K1, block_m, sorted_slot_ids,
+                       block_expert, num_padded, topk_w, ffn_ws, ffn_ws_bytes, stream);
   if (st != SRMOE_OK) return st;
   return moe_combine(T, K1, H, ffn_ws, ffn_ws_bytes, out, stream);
 }

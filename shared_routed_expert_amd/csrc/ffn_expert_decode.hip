@@ -1,0 +1,399 @@
+// Both expert GEMMs of a 16-row block in one workgroup (decode-shaped batches).
+//
+// A block is 16 sorted rows of one expert e. One 512-thread workgroup per block:
+//
+//  phase 1  gate/up: the block's 16 token rows of x_q go to LDS once; each of
+//           the 8 wavefronts owns NT = I / 64 tiles of 16 rows of w13[e] and
+//           streams them tile after tile in batches of 16 rows x 1 KB of K,
+//           one load instruction per row (1 KB contiguous: HBM streams runs
+//           like these faster than the same bytes as 8 rows x 128 B). A batch
+//           passes through the wavefront's LDS buffer in two 512-byte halves
+//           into the MFMA fragment layout (x is the A operand, the weight rows
+//           the B operand). Two batches are in flight per wavefront: while one
+//           is multiplied the next is loading.
+//  phase 2  g, u -> a = silu(g) * u -> FP8 a_q with the row (or row x 128-column
+//           group) absmax scale, in LDS; the row's output scale is its routing
+//           weight (times the FP8 scale per channel). a itself (float32) is also
+//           stored to the workspace, where the split kernels keep it.
+//  phase 3  down: each wavefront takes every eighth group of 64 output columns;
+//           a group's 64 rows of w2[e] are 64 * I contiguous bytes, loaded as
+//           1 KB runs and passed through LDS into the swap-AB fragment layout
+//           (weights as the A operand, a_q as B), the next group loading while
+//           one is multiplied. Weighted bf16 rows go to slot_out.
+//
+// The split kernels stream the same weights but pass a through HBM, quantise it in
+// a pass of their own and re-read it; here the down GEMM takes a_q from LDS and
+// one launch replaces three. All the block's work sits on one CU, so the ~160
+// workgroups of a decode batch stream side by side with eight wavefronts each
+// (enough loads in flight to keep HBM busy at that count).
+//
+// Weight loads go through buffer resources made per K step or column group
+// (scalar registers): a prefetch past the end gets a resource of zero length and
+// returns zeros without touching memory, so no load is predicated and the
+// compiler's memory waits stay exact. Everything the epilogues need per row or
+// column is fetched in the prologue: a load issued behind a prefetch can only be
+// waited for together with it.
+#include "common.hpp"
+
+namespace srmoe {
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kXMaxH = 5120;                    // largest H whose x rows fit the LDS budget
+constexpr int kXMaxHB = kXMaxH / kGroup;
+constexpr int kChunk = 1024;                    // K bytes of a phase-1 batch per row
+constexpr int kHalfRS = kChunk / 2 + 16;        // LDS row stride of a staged half batch
+
+// Raw buffer resource over [base, base + bytes) (GFX9 descriptor word 3); loads at
+// offsets past `bytes` return zero.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t slice_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ u32x4 bload(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+}
+
+template <int NT>
+struct ExpertDecodeLds {
+  static constexpr int I = NT * 64;
+  static constexpr int kX = 16 * (kXMaxH + 16);                 // x rows (phase 1)
+  static constexpr int kStage1 = 8 * 16 * kHalfRS;              // per-wavefront half batches (phase 1)
+  static constexpr int kGU = 16 * (2 * I + 4) * 4;              // g|u float32 (phase 1 -> 2)
+  static constexpr int kStage3 = 8 * 64 * (I + 16);             // per-wavefront w2 groups (phase 3)
+  static constexpr int kBig = (kX + kStage1) > kStage3 ? ((kX + kStage1) > kGU ? kX + kStage1 : kGU)
+                                                       : (kStage3 > kGU ? kStage3 : kGU);
+};
+
+template <bool kBlock, int NT>   // NT = I / 64
+__global__ void __launch_bounds__(512) expert_ffn_decode_kernel(
+    const uint8_t* __restrict__ xq, const float* __restrict__ sx, const uint8_t* __restrict__ w13,
+    const float* __restrict__ s13, const uint8_t* __restrict__ w2, const float* __restrict__ s2,
+    const int32_t* __restrict__ sorted, const int32_t* __restrict__ block_expert,
+    const float* __restrict__ topk_w, float* __restrict__ a_out, uint16_t* __restrict__ slot_out,
+    int T, int H, int K1) {
+  using Lds = ExpertDecodeLds<NT>;
+  constexpr int I = Lds::I;
+  constexpr int AS = I + 16;                // a_q row stride
+  constexpr int GS = 2 * I + 4;             // g|u row stride (floats)
+  constexpr int NI = I / 16;                // 1 KB runs per 64-row w2 group
+  constexpr int C = I / 32;                 // phase-2 columns per thread
+  __shared__ __align__(16) uint8_t big[Lds::kBig];
+  __shared__ __align__(16) uint8_t aqs[16 * AS];
+  __shared__ float rsc_s[16];
+  __shared__ float sa_s[16][2];
+  __shared__ int srow_s[16];
+  __shared__ float wgt_s[16];
+  __shared__ __align__(16) float sxs[kBlock ? kXMaxHB * 16 : 16];
+  __shared__ float s13s[kBlock ? (2 * I / kGroup) * kXMaxHB : 1];   // w13[e]'s block scales
+
+  const int b = blockIdx.x;
+  const int e = block_expert[b];   // -1 past the used rows
+  if (e < 0) return;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar loop control
+  const int r16 = lane & 15, kq = lane >> 4, r8 = lane >> 3;
+  const int sentinel = T * K1;
+  const uint64_t magic = slot_div_magic(K1);
+  const int HB = H / kGroup, nsteps = H / kGroup;
+  const int XS = H + 16;
+  uint8_t* xs = big;
+  uint8_t* stg1 = big + Lds::kX + wv * (16 * kHalfRS);
+
+  // ---- phase 1 prologue: per-row and per-column data, x rows into LDS, first weight batch
+  const uint8_t* w13e = w13 + (size_t)e * 2 * I * H;
+  const int tile0 = wv * NT;   // first of the wavefront's 16-row tiles of w13[e]
+  // Batch q = (tile pass q / nchunks, K chunk q % nchunks): row r of the tile is load r, at
+  // scalar offset r * H; lane l takes bytes 16 l .. 16 l + 15 of the chunk (an out-of-range
+  // offset, read as zero, past the end of a row). Batches past the last get a zero-length
+  // resource.
+  const int nchunks = (H + kChunk - 1) / kChunk;
+  const int nq = NT * nchunks;
+  auto batch_load = [&](int q, u32x4 (&L)[16]) __attribute__((always_inline)) {
+    const int n = q / nchunks, c = q - n * nchunks;
+    const bool in = q < nq;
+    const __amdgpu_buffer_rsrc_t r =
+        slice_rsrc(w13e + (in ? (size_t)16 * (tile0 + n) * H : 0), in ? (uint32_t)(16 * H) : 0u);
+    const int o = c * kChunk + lane * 16;
+    const uint32_t vo = o < H ? (uint32_t)o : 0x80000000u;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) L[i] = __builtin_amdgcn_raw_buffer_load_b128(r, (int)vo, i * H, 0);
+  };
+  float sc13[NT];
+#pragma unroll
+  for (int n = 0; n < NT; ++n) sc13[n] = kBlock ? 1.f : s13[(size_t)e * 2 * I + 16 * (tile0 + n) + r16];
+  if (tid < 16) {
+    const int s = sorted[b * 16 + tid];
+    srow_s[tid] = s;
+    wgt_s[tid] = s < sentinel ? topk_w[s] : 0.f;
+  }
+  if (kBlock) {
+    for (int i = tid; i < (2 * I / kGroup) * HB; i += 512) s13s[i] = s13[(size_t)e * (2 * I / kGroup) * HB + i];
+    for (int i = tid; i < 16 * HB; i += 512) {
+      const int r = i & 15, kb = i >> 4;
+      const int s = sorted[b * 16 + r];
+      sxs[i] = s < sentinel ? sx[(size_t)slot_token(s, magic) * HB + kb] : 0.f;
+    }
+  } else if (tid < 16) {
+    const int s = sorted[b * 16 + tid];
+    sxs[tid] = s < sentinel ? sx[slot_token(s, magic)] : 0.f;
+  }
+  u32x4 LA[16], LB[16];
+  {
+    // thread -> (row tid / 32, 16-byte chunks part, part + 32, ...); padding rows read token 0
+    const int xr = tid >> 5, part = tid & 31;
+    const int s_x = sorted[b * 16 + xr];
+    const int tx = s_x < sentinel ? slot_token(s_x, magic) : 0;
+    const uint8_t* src = xq + (size_t)tx * H;
+    constexpr int kMaxChunks = kXMaxH / 16 / 32;
+    u32x4 xv[kMaxChunks];
+#pragma unroll
+    for (int m = 0; m < kMaxChunks; ++m) {
+      const int c = part + 32 * m;
+      if (c < H / 16) xv[m] = *reinterpret_cast<const u32x4*>(src + c * 16);
+    }
+    // the first weight batch goes out behind the x rows, so that waiting for x leaves it in flight
+    batch_load(0, LA);
+#pragma unroll
+    for (int m = 0; m < kMaxChunks; ++m) {
+      const int c = part + 32 * m;
+      // opaque: a plain load-then-store pair would be merged into one copy placed at the store
+      asm volatile("" : "+v"(xv[m]));
+      if (c < H / 16) *reinterpret_cast<u32x4*>(xs + xr * XS + c * 16) = xv[m];
+    }
+  }
+  __syncthreads();
+
+  // ---- phase 1: gate/up
+  const v4f zero4 = {0.f, 0.f, 0.f, 0.f};
+  // cur accumulates the tile being streamed; at the end of a tile pass it is pushed onto
+  // acc[] (static register indices), which then holds the passes in order
+  v4f acc[NT], cur = zero4;
+#pragma unroll
+  for (int n = 0; n < NT; ++n) acc[n] = zero4;
+  auto process = [&](u32x4 (&L)[16], int q) __attribute__((always_inline)) {
+    const int n = q / nchunks, c = q - n * nchunks;
+    const int srow13 = (16 * (tile0 + n)) / kGroup;   // the tile's block row of w13[e]'s scales
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      if ((lane >> 5) == h) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) *reinterpret_cast<u32x4*>(stg1 + i * kHalfRS + (lane & 31) * 16) = L[i];
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        // past the end of K the weights read as zero; x stays on a real step (finite codes)
+        const int kb = min(c * 8 + h * 4 + j, nsteps - 1);
+        const v8i A = load32(xs + r16 * XS + kb * kGroup + kq * 32);
+        const v8i B = load32(stg1 + r16 * kHalfRS + j * kGroup + kq * 32);
+        if (!kBlock) {
+          cur = mfma_16x16x128_fp8(A, B, cur);
+        } else {
+          const v4f t = mfma_16x16x128_fp8(A, B, zero4);
+          const float sw = s13s[srow13 * HB + kb];
+          const float4 sxr = *reinterpret_cast<const float4*>(&sxs[kb * 16 + 4 * kq]);
+          cur[0] += t[0] * (sxr.x * sw);
+          cur[1] += t[1] * (sxr.y * sw);
+          cur[2] += t[2] * (sxr.z * sw);
+          cur[3] += t[3] * (sxr.w * sw);
+        }
+      }
+      // bounds how far the scheduler hoists fragment reads (registers: two batches are live)
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    asm volatile("" : "+v"(cur));   // the batch's MFMAs stay in the batch (not sunk into the next)
+    if (q < nq && c == nchunks - 1) {
+#pragma unroll
+      for (int m = 0; m + 1 < NT; ++m) acc[m] = acc[m + 1];
+      acc[NT - 1] = cur;
+      cur = zero4;
+    }
+  };
+#pragma unroll 1
+  for (int q = 0; q < nq; q += 2) {
+    batch_load(q + 1, LB);
+    __builtin_amdgcn_sched_barrier(0);
+    process(LA, q);
+    batch_load(q + 2, LA);
+    __builtin_amdgcn_sched_barrier(0);
+    process(LB, q + 1);
+  }
+
+  // ---- phase 3 prologue: the wavefront's first w2 group starts loading now
+  const int ng = H / 64;
+  const int n_my = (ng - wv + 7) >> 3;   // groups wv, wv + 8, ... below ng
+  const uint8_t* w2e = w2 + (size_t)e * H * I;
+  const float* s2e = s2 + (size_t)e * H;
+  // the wavefront's i-th group: its 64 rows of w2[e] and their 64 channel scales
+  auto load_group = [&](int i, u32x4 (&W)[NI], u32x4 (&S)[4]) __attribute__((always_inline)) {
+    const int g = wv + 8 * i;
+    const bool in = g < ng;
+    const __amdgpu_buffer_rsrc_t r = slice_rsrc(w2e + (in ? g * 64 * I : 0), in ? 64u * I : 0u);
+#pragma unroll
+    for (int j = 0; j < NI; ++j) W[j] = bload(r, (uint32_t)(j * 1024 + lane * 16));
+    if (!kBlock) {
+      const __amdgpu_buffer_rsrc_t rs = slice_rsrc(s2e + (in ? g * 64 : 0), in ? 256u : 0u);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) S[c] = bload(rs, (uint32_t)(kq * 64 + c * 16));
+    }
+  };
+  u32x4 WA[NI], WB[NI], SA[4], SB[4];
+  load_group(0, WA, SA);
+
+  // ---- phase 1 epilogue: scaled g|u tiles to LDS (x and the K-step buffers are free after the barrier)
+  __syncthreads();
+  float* gu = reinterpret_cast<float*>(big);
+#pragma unroll
+  for (int n = 0; n < NT; ++n) {
+    const int col = 16 * (tile0 + n) + r16;   // w13 row: gate for col < I, up above
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int row = 4 * kq + q;
+      gu[row * GS + col] = kBlock ? acc[n][q] : acc[n][q] * sxs[row] * sc13[n];
+    }
+  }
+  __syncthreads();
+
+  // ---- phase 2: a = silu(g) * u, FP8 with absmax scales
+  {
+    const int r = tid >> 5, part = tid & 31;
+    const bool valid = srow_s[r] < sentinel;
+    float av[C];
+    float amax = 0.f;
+#pragma unroll
+    for (int m = 0; m < C; ++m) {
+      const int c = part * C + m;
+      const float g = gu[r * GS + c], u = gu[r * GS + I + c];
+      av[m] = valid ? silu(g) * u : 0.f;
+      amax = fmaxf(amax, fabsf(av[m]));
+    }
+    // the float32 product also goes to the workspace (sorted-row order), where the split path keeps it
+    float* arow = a_out + (size_t)(b * 16 + r) * I + part * C;
+#pragma unroll
+    for (int m = 0; m < C; m += 2) *reinterpret_cast<float2*>(arow + m) = make_float2(av[m], av[m + 1]);
+    const float wgt = wgt_s[r];
+    // per channel: the row's 32 threads; block: the 128 / C threads of a 128-column group
+    const float scale = fp8_scale(group_max(amax, kBlock ? kGroup / C : 32));
+#pragma unroll
+    for (int m = 0; m < C; ++m) aqs[r * AS + part * C + m] = (uint8_t)e4m3_encode(__fdiv_rn(av[m], scale));
+    if (!kBlock) {
+      if (part == 0) rsc_s[r] = wgt * scale;
+    } else {
+      if (part == 0) rsc_s[r] = wgt;
+      if ((part * C) % kGroup == 0) sa_s[r][(part * C) / kGroup] = scale;
+    }
+  }
+  __syncthreads();
+
+  // ---- phase 3: down
+  uint8_t* stg3 = big + wv * 64 * AS;
+  uint32_t kc[2];
+  v8i avq[2];
+  float sr[2] = {0.f, 0.f};
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int koff = u * kGroup + kq * 32;
+    const bool in = koff < I;
+    kc[u] = in ? koff : I - 32;
+    const v8i t = load32(aqs + r16 * AS + kc[u]);
+    const v8i zero8 = {0, 0, 0, 0, 0, 0, 0, 0};
+    avq[u] = in ? t : zero8;
+    if (kBlock && u * kGroup < I) sr[u] = sa_s[r16][u];
+  }
+  const float rsc = rsc_s[r16];
+  const int srow = srow_s[r16];
+  // lane's LDS slot for each 16-byte piece of a group: column c = o / I of the 64 goes to
+  // row 16 ((c / 4) % 4) + 4 (c / 16) + c % 4 so that MFMA tile n reads rows 16 n .. 16 n + 15
+  int soff[NI];
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int o = i * 1024 + lane * 16;
+    const int c = o / I, byte = o - c * I;
+    soff[i] = (16 * ((c >> 2) & 3) + 4 * (c >> 4) + (c & 3)) * AS + byte;
+  }
+  auto down_group = [&](u32x4 (&W)[NI], u32x4 (&S)[4], int i) __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < NI; ++j) *reinterpret_cast<u32x4*>(stg3 + soff[j]) = W[j];
+    v4f d[4] = {zero4, zero4, zero4, zero4};
+#pragma unroll
+    for (int u = 0; u < (I > kGroup ? 2 : 1); ++u) {
+      v8i bw[4];
+#pragma unroll
+      for (int n = 0; n < 4; ++n) bw[n] = load32(stg3 + (16 * n + r16) * AS + kc[u]);
+      if (!kBlock) {
+#pragma unroll
+        for (int n = 0; n < 4; ++n) d[n] = mfma_16x16x128_fp8(bw[n], avq[u], d[n]);
+      } else {
+        // a group's 64 columns lie in one 128-column block of w2's scales
+        const int g = min(wv + 8 * i, ng - 1);
+        const float swb = s2[((size_t)e * (H / kGroup) + (g * 64) / kGroup) * (I / kGroup) + u];
+        const float f = sr[u] * swb;
+#pragma unroll
+        for (int n = 0; n < 4; ++n) {
+          const v4f t = mfma_16x16x128_fp8(bw[n], avq[u], zero4);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) d[n][q] += t[q] * f;
+        }
+      }
+    }
+    // the MFMAs read operands across the whole wavefront: keep them ahead of the exits below
+#pragma unroll
+    for (int n = 0; n < 4; ++n) asm volatile("" : "+v"(d[n]));
+    const int h0 = (wv + 8 * i) * 64;
+    if (h0 >= H || srow >= sentinel) return;
+    float sw[16];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      sw[4 * c] = kBlock ? 1.f : __uint_as_float(S[c].x);
+      sw[4 * c + 1] = kBlock ? 1.f : __uint_as_float(S[c].y);
+      sw[4 * c + 2] = kBlock ? 1.f : __uint_as_float(S[c].z);
+      sw[4 * c + 3] = kBlock ? 1.f : __uint_as_float(S[c].w);
+    }
+    uint32_t packed[8];
+#pragma unroll
+    for (int c = 0; c < 16; c += 2) {   // column c = 4 n + q of the lane's 16
+      const float y0 = d[c >> 2][c & 3] * sw[c] * rsc;
+      const float y1 = d[(c + 1) >> 2][(c + 1) & 3] * sw[c + 1] * rsc;
+      packed[c >> 1] = (uint32_t)f32_to_bf16(y0) | ((uint32_t)f32_to_bf16(y1) << 16);
+    }
+    uint4* dst = reinterpret_cast<uint4*>(slot_out + (size_t)srow * H + h0 + kq * 16);
+    dst[0] = make_uint4(packed[0], packed[1], packed[2], packed[3]);
+    dst[1] = make_uint4(packed[4], packed[5], packed[6], packed[7]);
+  };
+#pragma unroll 1
+  for (int i = 0; i < n_my; i += 2) {
+    load_group(i + 1, WB, SB);
+    __builtin_amdgcn_sched_barrier(0);
+    down_group(WA, SA, i);
+    load_group(i + 2, WA, SA);
+    __builtin_amdgcn_sched_barrier(0);
+    down_group(WB, SB, i + 1);
+  }
+}
+
+bool expert_ffn_decode_supported(int H, int I) {
+  return I % 64 == 0 && I >= 64 && I <= 256 && H % kGroup == 0 && H <= kXMaxH;
+}
+
+hipError_t launch_expert_ffn_decode(const uint8_t* xq, const float* sx, const uint8_t* w13,
+                                    const float* s13, const uint8_t* w2, const float* s2, bool block,
+                                    const int32_t* sorted, const int32_t* block_expert,
+                                    const float* topk_w, float* a_out, uint16_t* slot_out, int T,
+                                    int H, int I, int E1, int K1, hipStream_t stream) {
+  const int P_max = (int)sorted_capacity(T, K1, E1, 16);
+  const dim3 grid(P_max / 16), blk(512);
+#define SRMOE_EFD(B, N)                                                                              \
+  hipLaunchKernelGGL((expert_ffn_decode_kernel<B, N>), grid, blk, 0, stream, xq, sx, w13, s13, w2, s2, \
+                     sorted, block_expert, topk_w, a_out, slot_out, T, H, K1)
+#define SRMOE_EFD2(N) if (block) SRMOE_EFD(true, N); else SRMOE_EFD(false, N); break;
+  switch (I / 64) {
+    case 1: SRMOE_EFD2(1)
+    case 2: SRMOE_EFD2(2)
+    case 3: SRMOE_EFD2(3)
+    default: SRMOE_EFD2(4)
+  }
+#undef SRMOE_EFD2
+#undef SRMOE_EFD
+  return hipGetLastError();
+}
+
+}  // namespace srmoe

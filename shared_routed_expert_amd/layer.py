@@ -74,12 +74,27 @@ class FusedMoE:
                         self.sorted_slot_ids, self.block_expert, self.num_padded, self.topk_w,
                         self.ws, self.ws_bytes, stream)
 
-    def ffn_stages(self, x, W: DeviceWeights, stream=None, between=None):
-        """The FFN as its three C stages; `between(name)` is called after each launch."""
+    def one_kernel_experts(self):
+        """True when moe_ffn_experts runs gate/up, SwiGLU, a's quantisation and down as one kernel."""
+        return L.moe_ffn_experts_one_kernel(self.H, self.I, self.block_m)
+
+    def ffn_stage_names(self, split=False):
+        return ["quant_x", "gate_up", "down"] if split or not self.one_kernel_experts() else ["quant_x", "experts"]
+
+    def ffn_stages(self, x, W: DeviceWeights, stream=None, between=None, split=False):
+        """The FFN as separate C stages (ffn_stage_names); `between(name)` is called after each
+        launch. split=True always takes moe_ffn_gate_up + moe_ffn_down for the expert GEMMs."""
         T, H, I, E1, K1, bm = self.dims()
         L.moe_ffn_quant_x(x, self.scale_mode, T, H, I, E1, K1, bm, self.ws, self.ws_bytes, stream)
         if between:
             between("quant_x")
+        if not split and self.one_kernel_experts():
+            L.moe_ffn_experts(W.w13, W.s13, W.w2, W.s2, self.scale_mode, T, H, I, E1, K1, bm,
+                              self.sorted_slot_ids, self.block_expert, self.num_padded, self.topk_w,
+                              self.ws, self.ws_bytes, stream)
+            if between:
+                between("experts")
+            return
         L.moe_ffn_gate_up(W.w13, W.s13, self.scale_mode, T, H, I, E1, K1, bm, self.sorted_slot_ids,
                           self.block_expert, self.num_padded, self.ws, self.ws_bytes, stream)
         if between:

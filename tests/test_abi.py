@@ -155,6 +155,30 @@ def test_ffn_stage_rejects(L):
     del a
 
 
+def test_ffn_experts_rejects(L):
+    def f(**kw):
+        args = dict(w13=FAKE, s13=FAKE, w2=FAKE, s2=FAKE, scale_mode=0, T=64, H=5120, I=192, E1=161, K1=9,
+                    block_m=16, sorted_slot_ids=FAKE, block_expert=FAKE, num_padded=FAKE, topk_w=FAKE,
+                    workspace=FAKE, ws_bytes=1 << 40)
+        args.update(kw)
+        return L.moe_ffn_experts(**args, stream=0, check=False)
+    for name in ("w13", "s13", "w2", "s2", "sorted_slot_ids", "block_expert", "num_padded", "topk_w",
+                 "workspace"):
+        assert f(**{name: None}) == -1, name
+        assert f(**{name: MIS}) == -1, name
+    assert f(I=100) == -2 and f(block_m=8) == -2 and f(scale_mode=1, I=192) == -2
+    assert f(ws_bytes=L.moe_ffn_workspace_bytes(64, 5120, 192, 161, 9, 16, 0) - 1) == -3
+    assert f(T=0, w13=None) == 0
+
+
+def test_ffn_experts_one_kernel_shapes(L):
+    one = L.moe_ffn_experts_one_kernel
+    # 16-row blocks, I a multiple of 64 in 64..256, H <= 5120 (the x rows of a block live in LDS)
+    assert one(5120, 192, 16) and one(5120, 64, 16) and one(256, 256, 16) and one(384, 128, 16)
+    assert not one(5120, 192, 32) and not one(5120, 96, 16) and not one(5120, 320, 16)
+    assert not one(5248, 192, 16) and not one(5120, 32, 16)
+
+
 def test_combine_rejects(L):
     f = lambda *a: L.moe_combine(*a, stream=0, check=False)
     assert f(-1, 9, 5120, FAKE, 1 << 30, FAKE) == -1

@@ -107,6 +107,34 @@ def test_ffn_small(name, bm):
     check_outputs(inp, layer)
 
 
+# Shapes where moe_ffn_experts runs as one kernel (16-row blocks, I a multiple of 64 up to
+# 256, H <= 5120); forward() takes that kernel there, and the split kernels (gate/up, the
+# separate quantisation of a, down) must stay correct at the same shapes. i192 has an odd
+# number of K-step batches and of 64-column groups per wavefront.
+ONE_KERNEL = {
+    "one_token": SMALL["one_token"],
+    "block": SMALL["block"],
+    "multigroup": small_cfg("multigroup", T=64, H=256, I=128, E=4, K=2, seed=24),
+    "i192": small_cfg("i192", T=48, H=640, I=192, E=12, K=4, seed=26),
+}
+
+
+@pytest.mark.parametrize("split", [False, True])
+@pytest.mark.parametrize("name", list(ONE_KERNEL))
+def test_ffn_decode_blocks_both_routes(name, split):
+    inp = generate(ONE_KERNEL[name])
+    note(f"ffn {name} bm=16 split={split}")
+    layer, W = make_layer(inp, 16)
+    assert layer.one_kernel_experts()
+    layer.route(to_dev(inp.logits), 1.0)
+    layer.align()
+    layer.ffn_stages(bf16_dev(inp.x_bf16), W, split=split)
+    layer.combine()
+    torch.cuda.synchronize()
+    check_stages(inp, layer)
+    check_outputs(inp, layer)
+
+
 def test_ffn_determinism():
     inp = generate(SMALL["ragged_wide"])
     layer, W = run_layer(inp, 32)
