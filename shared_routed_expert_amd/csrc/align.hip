@@ -1,6 +1,6 @@
 // Align / sort / pad of the (token, slot) entries by expert: a stable counting sort.
 //
-// The T*K1 flat entries s = t*K1 + k are cut into chunks of 1024, one
+// The T*K1 flat entries s = t*K1 + k are cut into chunks of 256, one
 // wavefront per chunk. Inside a chunk, 64 entries at a time, lanes holding the
 // same expert find each other with 8 ballots over the bits of the expert id;
 // a lane's rank among them is the popcount of the lower lanes in that set, and
@@ -10,14 +10,16 @@
 // sentinel T*K1. Nothing depends on atomics or scheduling, so the output is
 // the unique stable order.
 //
-// Small inputs (<= 4 chunks) run as one workgroup whose 4 wavefronts take
+// Small inputs (<= 4096 entries) run as one workgroup whose 4 wavefronts take
 // consecutive quarters of the entries; larger ones as count -> scan -> scatter.
 #include "front_dev.hpp"
 
 namespace srmoe {
 
-constexpr int kChunk = 1024;             // entries per wavefront chunk in the large path
-constexpr int kPerLane = kChunk / kWave;   // 16 entries of a chunk per lane
+constexpr int kSmallMax = 4096;                 // entries handled by the one-workgroup path
+constexpr int kSmallPerLane = kSmallMax / 256;   // 16 per lane there
+constexpr int kChunk = 256;                      // entries per wavefront chunk in the large path
+constexpr int kPerLane = kChunk / kWave;         // 4 entries of a chunk per lane
 
 __global__ void __launch_bounds__(256) align_small_kernel(
     const int32_t* __restrict__ ids, int N, int E1, int block_m, int P_max,
@@ -26,8 +28,8 @@ __global__ void __launch_bounds__(256) align_small_kernel(
   __shared__ int cnt[4][kMaxE1];
   __shared__ int off[kMaxE1];
   __shared__ int wsum[16];
-  align_in_workgroup<kPerLane>(ids, N, E1, block_m, P_max, cnt, off, wsum, sorted, block_expert,
-                               counts, offsets, num_padded);
+  align_in_workgroup<kSmallPerLane>(ids, N, E1, block_m, P_max, cnt, off, wsum, sorted,
+                                    block_expert, counts, offsets, num_padded);
 }
 
 // Large inputs. Pass 1: per-chunk counts -> chunk_counts[chunk][E1].
@@ -49,7 +51,11 @@ __global__ void __launch_bounds__(256) align_count_kernel(const int32_t* __restr
 }
 
 // Pass 2 (one workgroup): totals, padded offsets, outputs, fills; chunk_counts
-// becomes each chunk's first output position per expert.
+// becomes each chunk's first output position per expert. Thread e walks expert e's
+// column of chunk_counts kScanU chunks at a time, all of a group's loads issued before
+// they are used (one load per iteration would wait on memory once per chunk).
+constexpr int kScanU = 16;
+
 __global__ void __launch_bounds__(256) align_scan_kernel(
     int N, int E1, int block_m, int P_max, int32_t* __restrict__ chunk_counts,
     int32_t* __restrict__ sorted, int32_t* __restrict__ block_expert,
@@ -60,16 +66,27 @@ __global__ void __launch_bounds__(256) align_scan_kernel(
   const int e = threadIdx.x;
   int total_e = 0;
   if (e < E1)
-    for (int c = 0; c < nchunks; ++c) total_e += chunk_counts[(size_t)c * E1 + e];
+    for (int c0 = 0; c0 < nchunks; c0 += kScanU) {
+      int v[kScanU];
+#pragma unroll
+      for (int u = 0; u < kScanU; ++u) v[u] = c0 + u < nchunks ? chunk_counts[(size_t)(c0 + u) * E1 + e] : 0;
+#pragma unroll
+      for (int u = 0; u < kScanU; ++u) total_e += v[u];
+    }
   finish_layout(e, E1, block_m, total_e, N, P_max, off, wsum, sorted, block_expert, counts, offsets,
                 num_padded);
   __syncthreads();
   if (e < E1) {
     int run = off[e];
-    for (int c = 0; c < nchunks; ++c) {
-      const int n = chunk_counts[(size_t)c * E1 + e];
-      chunk_counts[(size_t)c * E1 + e] = run;
-      run += n;
+    for (int c0 = 0; c0 < nchunks; c0 += kScanU) {
+      int v[kScanU];
+#pragma unroll
+      for (int u = 0; u < kScanU; ++u) v[u] = c0 + u < nchunks ? chunk_counts[(size_t)(c0 + u) * E1 + e] : 0;
+#pragma unroll
+      for (int u = 0; u < kScanU; ++u) {
+        if (c0 + u < nchunks) chunk_counts[(size_t)(c0 + u) * E1 + e] = run;
+        run += v[u];
+      }
     }
   }
 }
@@ -104,7 +121,7 @@ hipError_t launch_align(const int32_t* ids, int T, int K1, int E1, int block_m, 
   const int N = T * K1;
   const int P_max = (int)sorted_capacity(T, K1, E1, block_m);
   const int nchunks = (N + kChunk - 1) / kChunk;
-  if (nchunks <= 4) {
+  if (N <= kSmallMax) {
     hipLaunchKernelGGL(align_small_kernel, dim3(1), dim3(256), 0, stream, ids, N, E1, block_m, P_max,
                        sorted, block_expert, counts, offsets, num_padded);
     return hipGetLastError();

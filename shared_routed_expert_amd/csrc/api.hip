@@ -25,10 +25,18 @@ hipError_t launch_gate_up_decode(const uint8_t*, const float*, const uint8_t*, c
 hipError_t launch_layer_front(const float*, int, int, int, float, int32_t*, float*, const uint16_t*,
                               int, bool, uint8_t*, float*, hipStream_t);
 bool expert_ffn_decode_supported(int H, int I);
+bool expert_ffn_decode_align_supported(int T, int K1);
+struct AlignOut {
+  const int32_t* topk_ids;
+  int32_t* counts;
+  int32_t* offsets;
+  int32_t* num_padded;
+  int E1;
+};
 hipError_t launch_expert_ffn_decode(const uint8_t*, const float*, const uint8_t*, const float*,
-                                    const uint8_t*, const float*, bool, const int32_t*, const int32_t*,
-                                    const float*, float*, uint16_t*, int, int, int, int, int,
-                                    hipStream_t);
+                                    const uint8_t*, const float*, bool, int32_t*, int32_t*,
+                                    const AlignOut*, const float*, float*, uint16_t*, int, int, int,
+                                    int, int, hipStream_t);
 }  // namespace srmoe
 
 using namespace srmoe;
@@ -267,11 +275,12 @@ int moe_ffn_experts(const uint8_t* w13, const float* s13, const uint8_t* w2, con
                         num_padded, topk_w, workspace, ws_bytes, stream);
   }
   char* ws = static_cast<char*>(workspace);
+  // sorted_slot_ids / block_expert are only read when no align output is requested
   return hip_status(launch_expert_ffn_decode(
       reinterpret_cast<const uint8_t*>(ws + L.xq), reinterpret_cast<const float*>(ws + L.sx), w13, s13,
-      w2, s2, scale_mode == SRMOE_SCALE_BLOCK128, sorted_slot_ids, block_expert, topk_w,
-      reinterpret_cast<float*>(ws + L.a), reinterpret_cast<uint16_t*>(ws + L.slot_out), T, H, I, E1,
-      K1, as_stream(stream)));
+      w2, s2, scale_mode == SRMOE_SCALE_BLOCK128, const_cast<int32_t*>(sorted_slot_ids),
+      const_cast<int32_t*>(block_expert), nullptr, topk_w, reinterpret_cast<float*>(ws + L.a),
+      reinterpret_cast<uint16_t*>(ws + L.slot_out), T, H, I, E1, K1, as_stream(stream)));
 }
 
 int moe_fused_ffn(const uint16_t* x, const uint8_t* w13, const float* s13, const uint8_t* w2,
@@ -325,6 +334,18 @@ int moe_layer_forward(const uint16_t* x, const float* logits, const uint8_t* w13
                                      reinterpret_cast<uint8_t*>(ws + L.xq),
                                      reinterpret_cast<float*>(ws + L.sx), sm));
   if (st != SRMOE_OK) return st;
+  if (moe_ffn_experts_one_kernel(H, I, block_m) && expert_ffn_decode_align_supported(T, K1)) {
+    // decode shapes: the expert kernel derives the align layout itself (every workgroup
+    // from topk_ids) and writes the align outputs, so the layer is three launches
+    const AlignOut al{topk_ids, expert_counts, expert_offsets, num_padded, E1};
+    st = hip_status(launch_expert_ffn_decode(
+        reinterpret_cast<const uint8_t*>(ws + L.xq), reinterpret_cast<const float*>(ws + L.sx), w13,
+        s13, w2, s2, blk, sorted_slot_ids, block_expert, &al, topk_w,
+        reinterpret_cast<float*>(ws + L.a), reinterpret_cast<uint16_t*>(ws + L.slot_out), T, H, I,
+        E1, K1, sm));
+    if (st != SRMOE_OK) return st;
+    return moe_combine(T, K1, H, ffn_ws, ffn_ws_bytes, out, stream);
+  }
   st = moe_align_by_expert(topk_ids, T, K1, E1, block_m, sorted_slot_ids, block_expert, expert_counts,
                            expert_offsets, num_padded, align_ws, align_ws_bytes, stream);
   if (st != SRMOE_OK) return st;

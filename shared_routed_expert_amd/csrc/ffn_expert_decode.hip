@@ -41,8 +41,8 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kXMaxH = 5120;                    // largest H whose x rows fit the LDS budget
 constexpr int kXMaxHB = kXMaxH / kGroup;
-constexpr int kChunk = 1024;                    // K bytes of a phase-1 batch per row
-constexpr int kHalfRS = kChunk / 2 + 16;        // LDS row stride of a staged half batch
+constexpr int kRunK = 1024;                     // K bytes of a phase-1 batch per row
+constexpr int kHalfRS = kRunK / 2 + 16;         // LDS row stride of a staged half batch
 
 // Raw buffer resource over [base, base + bytes) (GFX9 descriptor word 3); loads at
 // offsets past `bytes` return zero.
@@ -68,11 +68,23 @@ struct ExpertDecodeLds {
                                                        : (kStage3 > kGU ? kStage3 : kGU);
 };
 
-template <bool kBlock, int NT>   // NT = I / 64
+// The in-kernel align (kAlign): every workgroup derives the expert-sorted layout of
+// the T*K1 <= kAlignMaxN routed entries itself and writes its share of the align
+// outputs (see the prologue).
+constexpr int kAlignMaxN = 4096;
+struct AlignOut {
+  const int32_t* topk_ids;   // [T*K1] in
+  int32_t* counts;           // [E1] out (workgroup 0)
+  int32_t* offsets;          // [E1+1] out (workgroup 0)
+  int32_t* num_padded;       // [1] out (workgroup 0)
+  int E1;
+};
+
+template <bool kBlock, int NT, bool kAlign>   // NT = I / 64
 __global__ void __launch_bounds__(512) expert_ffn_decode_kernel(
     const uint8_t* __restrict__ xq, const float* __restrict__ sx, const uint8_t* __restrict__ w13,
     const float* __restrict__ s13, const uint8_t* __restrict__ w2, const float* __restrict__ s2,
-    const int32_t* __restrict__ sorted, const int32_t* __restrict__ block_expert,
+    int32_t* __restrict__ sorted, int32_t* __restrict__ block_expert, AlignOut al,
     const float* __restrict__ topk_w, float* __restrict__ a_out, uint16_t* __restrict__ slot_out,
     int T, int H, int K1) {
   using Lds = ExpertDecodeLds<NT>;
@@ -91,8 +103,6 @@ __global__ void __launch_bounds__(512) expert_ffn_decode_kernel(
   __shared__ float s13s[kBlock ? (2 * I / kGroup) * kXMaxHB : 1];   // w13[e]'s block scales
 
   const int b = blockIdx.x;
-  const int e = block_expert[b];   // -1 past the used rows
-  if (e < 0) return;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar loop control
   const int r16 = lane & 15, kq = lane >> 4, r8 = lane >> 3;
@@ -103,6 +113,104 @@ __global__ void __launch_bounds__(512) expert_ffn_decode_kernel(
   uint8_t* xs = big;
   uint8_t* stg1 = big + Lds::kX + wv * (16 * kHalfRS);
 
+  // ---- the block: its expert e (-1 past the used rows) and its 16 sorted rows -> srow_s
+  int e;
+  if (!kAlign) {
+    e = block_expert[b];
+    if (e < 0) return;
+    if (tid < 16) srow_s[tid] = sorted[b * 16 + tid];
+  } else {
+    // The layout of the align call, derived here from topk_ids: per-expert counts
+    // (LDS atomics; counts do not depend on their order), each expert's segment padded
+    // to 16 rows in ascending expert order, then the block's rows = the entries of its
+    // expert ranked 16 (b - first block) .. + 15 in flat-slot order (ballots), padding
+    // rows = the sentinel. Entry s = 512 j + tid is held by thread tid.
+    __shared__ int e_s;
+    int* cnt_l = reinterpret_cast<int*>(big);   // [256]
+    int* pad_l = cnt_l + 256;                   // [256] first row of each expert
+    int* wc_l = pad_l + 256;                    // [8][8] entries of e per (j, wavefront)
+    constexpr int kJ = kAlignMaxN / 512;
+    int idv[kJ];
+#pragma unroll
+    for (int j = 0; j < kJ; ++j) idv[j] = 512 * j + tid < sentinel ? al.topk_ids[512 * j + tid] : -1;
+    if (tid < 256) cnt_l[tid] = 0;
+    if (tid < 16) srow_s[tid] = sentinel;
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < kJ; ++j)
+      if (idv[j] >= 0) atomicAdd(&cnt_l[idv[j]], 1);
+    __syncthreads();
+    if (wv == 0) {   // exclusive scan of the padded counts, 4 experts per lane
+      int pc[4], sum = 0;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int ex = lane * 4 + u;
+        pc[u] = ex < al.E1 ? (cnt_l[ex] + 15) & ~15 : 0;
+        sum += pc[u];
+      }
+      int inc = sum;
+#pragma unroll
+      for (int o = 1; o < kWave; o <<= 1) {
+        const int n = __shfl_up(inc, o, kWave);
+        if (lane >= o) inc += n;
+      }
+      const int total = __shfl(inc, kWave - 1, kWave);
+      int run = inc - sum;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int ex = lane * 4 + u;
+        if (ex < al.E1) {
+          pad_l[ex] = run;
+          if (b == 0) {
+            al.counts[ex] = cnt_l[ex];
+            al.offsets[ex] = run;
+          }
+        }
+        if (pc[u] > 0 && b * 16 >= run && b * 16 < run + pc[u]) e_s = ex;
+        run += pc[u];
+      }
+      if (lane == 0) {
+        if (b * 16 >= total) e_s = -1;
+        if (b == 0) {
+          al.offsets[al.E1] = total;
+          al.num_padded[0] = total;
+        }
+      }
+    }
+    __syncthreads();
+    e = e_s;
+    if (e >= 0) {
+      const int first = b * 16 - pad_l[e];   // rank of the block's first row within e
+      const uint64_t lower = (1ull << lane) - 1ull;
+      uint64_t m[kJ];
+#pragma unroll
+      for (int j = 0; j < kJ; ++j) {
+        m[j] = __ballot(idv[j] == e);
+        if (lane == 0) wc_l[j * 8 + wv] = __popcll(m[j]);
+      }
+      __syncthreads();
+      int before = 0;   // entries of e in (j, wavefront) pairs ahead of this one
+#pragma unroll
+      for (int j = 0; j < kJ; ++j) {
+        int mine = before;
+        for (int w = 0; w < 8; ++w) {
+          const int c = wc_l[j * 8 + w];
+          mine += w < wv ? c : 0;
+          before += c;
+        }
+        if (idv[j] == e) {
+          const int r = mine + __popcll(m[j] & lower) - first;
+          if (r >= 0 && r < 16) srow_s[r] = 512 * j + tid;
+        }
+      }
+    }
+    __syncthreads();
+    if (tid < 16) sorted[b * 16 + tid] = srow_s[tid];
+    if (tid == 0) block_expert[b] = e;
+    if (e < 0) return;
+  }
+  __syncthreads();
+
   // ---- phase 1 prologue: per-row and per-column data, x rows into LDS, first weight batch
   const uint8_t* w13e = w13 + (size_t)e * 2 * I * H;
   const int tile0 = wv * NT;   // first of the wavefront's 16-row tiles of w13[e]
@@ -110,14 +218,14 @@ __global__ void __launch_bounds__(512) expert_ffn_decode_kernel(
   // scalar offset r * H; lane l takes bytes 16 l .. 16 l + 15 of the chunk (an out-of-range
   // offset, read as zero, past the end of a row). Batches past the last get a zero-length
   // resource.
-  const int nchunks = (H + kChunk - 1) / kChunk;
+  const int nchunks = (H + kRunK - 1) / kRunK;
   const int nq = NT * nchunks;
   auto batch_load = [&](int q, u32x4 (&L)[16]) __attribute__((always_inline)) {
     const int n = q / nchunks, c = q - n * nchunks;
     const bool in = q < nq;
     const __amdgpu_buffer_rsrc_t r =
         slice_rsrc(w13e + (in ? (size_t)16 * (tile0 + n) * H : 0), in ? (uint32_t)(16 * H) : 0u);
-    const int o = c * kChunk + lane * 16;
+    const int o = c * kRunK + lane * 16;
     const uint32_t vo = o < H ? (uint32_t)o : 0x80000000u;
 #pragma unroll
     for (int i = 0; i < 16; ++i) L[i] = __builtin_amdgcn_raw_buffer_load_b128(r, (int)vo, i * H, kWeightPolicy);
@@ -126,26 +234,25 @@ __global__ void __launch_bounds__(512) expert_ffn_decode_kernel(
 #pragma unroll
   for (int n = 0; n < NT; ++n) sc13[n] = kBlock ? 1.f : s13[(size_t)e * 2 * I + 16 * (tile0 + n) + r16];
   if (tid < 16) {
-    const int s = sorted[b * 16 + tid];
-    srow_s[tid] = s;
+    const int s = srow_s[tid];
     wgt_s[tid] = s < sentinel ? topk_w[s] : 0.f;
   }
   if (kBlock) {
     for (int i = tid; i < (2 * I / kGroup) * HB; i += 512) s13s[i] = s13[(size_t)e * (2 * I / kGroup) * HB + i];
     for (int i = tid; i < 16 * HB; i += 512) {
       const int r = i & 15, kb = i >> 4;
-      const int s = sorted[b * 16 + r];
+      const int s = srow_s[r];
       sxs[i] = s < sentinel ? sx[(size_t)slot_token(s, magic) * HB + kb] : 0.f;
     }
   } else if (tid < 16) {
-    const int s = sorted[b * 16 + tid];
+    const int s = srow_s[tid];
     sxs[tid] = s < sentinel ? sx[slot_token(s, magic)] : 0.f;
   }
   u32x4 LA[16], LB[16];
   {
     // thread -> (row tid / 32, 16-byte chunks part, part + 32, ...); padding rows read token 0
     const int xr = tid >> 5, part = tid & 31;
-    const int s_x = sorted[b * 16 + xr];
+    const int s_x = srow_s[xr];
     const int tx = s_x < sentinel ? slot_token(s_x, magic) : 0;
     const uint8_t* src = xq + (size_t)tx * H;
     constexpr int kMaxChunks = kXMaxH / 16 / 32;
@@ -377,18 +484,31 @@ __global__ void __launch_bounds__(512) expert_ffn_decode_kernel(
 bool expert_ffn_decode_supported(int H, int I) {
   return I % 64 == 0 && I >= 64 && I <= 256 && H % kGroup == 0 && H <= kXMaxH;
 }
+bool expert_ffn_decode_align_supported(int T, int K1) { return (size_t)T * K1 <= kAlignMaxN; }
 
+// align == nullptr: sorted / block_expert are inputs (from the align call). Otherwise
+// the kernel derives them from align->topk_ids and writes them with the other align
+// outputs (T*K1 <= kAlignMaxN).
 hipError_t launch_expert_ffn_decode(const uint8_t* xq, const float* sx, const uint8_t* w13,
                                     const float* s13, const uint8_t* w2, const float* s2, bool block,
-                                    const int32_t* sorted, const int32_t* block_expert,
+                                    int32_t* sorted, int32_t* block_expert, const AlignOut* align,
                                     const float* topk_w, float* a_out, uint16_t* slot_out, int T,
                                     int H, int I, int E1, int K1, hipStream_t stream) {
   const int P_max = (int)sorted_capacity(T, K1, E1, 16);
   const dim3 grid(P_max / 16), blk(512);
-#define SRMOE_EFD(B, N)                                                                              \
-  hipLaunchKernelGGL((expert_ffn_decode_kernel<B, N>), grid, blk, 0, stream, xq, sx, w13, s13, w2, s2, \
-                     sorted, block_expert, topk_w, a_out, slot_out, T, H, K1)
-#define SRMOE_EFD2(N) if (block) SRMOE_EFD(true, N); else SRMOE_EFD(false, N); break;
+  const AlignOut al = align ? *align : AlignOut{nullptr, nullptr, nullptr, nullptr, E1};
+#define SRMOE_EFD(B, N, A)                                                                          \
+  hipLaunchKernelGGL((expert_ffn_decode_kernel<B, N, A>), grid, blk, 0, stream, xq, sx, w13, s13, w2, \
+                     s2, sorted, block_expert, al, topk_w, a_out, slot_out, T, H, K1)
+#define SRMOE_EFD2(N)                              \
+  if (block) {                                     \
+    if (align) SRMOE_EFD(true, N, true);           \
+    else SRMOE_EFD(true, N, false);                \
+  } else {                                         \
+    if (align) SRMOE_EFD(false, N, true);          \
+    else SRMOE_EFD(false, N, false);               \
+  }                                                \
+  break;
   switch (I / 64) {
     case 1: SRMOE_EFD2(1)
     case 2: SRMOE_EFD2(2)
