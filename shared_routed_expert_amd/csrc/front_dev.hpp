@@ -243,8 +243,10 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* excl, int* wsum)
   return total;
 }
 
-// Expert totals -> padded offsets, the outputs, and the padding/tail fills. Thread e
-// owns expert e (< E1 <= 256). off[e] (LDS) receives expert e's first row.
+// Expert totals -> padded offsets and the outputs. Thread e owns expert e (< E1 <= 256).
+// off[e] (LDS) receives expert e's first row. `sorted` and `block_expert` must already
+// hold the sentinel / -1 everywhere (fill_layout): only the used blocks' experts are
+// written here, the entries by the scatter.
 __device__ __forceinline__ void finish_layout(int e, int E1, int block_m, int total_e, int sentinel,
                                               int P_max, int* off, int* wsum,
                                               int32_t* __restrict__ sorted,
@@ -259,15 +261,22 @@ __device__ __forceinline__ void finish_layout(int e, int E1, int block_m, int to
     off[e] = excl;
     counts[e] = total_e;
     offsets[e] = excl;
-    for (int r = excl + total_e; r < excl + padded; ++r) sorted[r] = sentinel;
     for (int b = excl / block_m; b < (excl + padded) / block_m; ++b) block_expert[b] = e;
   }
   if (threadIdx.x == 0) {
     offsets[E1] = total;
     num_padded[0] = total;
   }
-  for (int r = total + threadIdx.x; r < P_max; r += blockDim.x) sorted[r] = sentinel;
-  for (int b = total / block_m + threadIdx.x; b < P_max / block_m; b += blockDim.x) block_expert[b] = -1;
+}
+
+// Every row of `sorted` := sentinel, every entry of `block_expert` := -1, with coalesced
+// stores by `nthreads` threads numbered i (the padding rows and unused blocks keep these
+// values; the align writes the rest afterwards).
+__device__ __forceinline__ void fill_layout(int i, int nthreads, int sentinel, int block_m, int P_max,
+                                            int32_t* __restrict__ sorted,
+                                            int32_t* __restrict__ block_expert) {
+  for (int r = i; r < P_max; r += nthreads) sorted[r] = sentinel;
+  for (int b = i; b < P_max / block_m; b += nthreads) block_expert[b] = -1;
 }
 
 // Whole align of N <= 64 * kPer * (blockDim/64) entries inside one workgroup: the
@@ -287,6 +296,7 @@ __device__ __forceinline__ void align_in_workgroup(const int32_t* ids, int N, in
   const int start = min(wv * per, N), end = min(start + per, N);
   int ev[kPer];
   load_chunk<kPer>(ids, start, end, ev);
+  fill_layout(threadIdx.x, blockDim.x, N, block_m, P_max, sorted, block_expert);
   for (int i = threadIdx.x; i < nw * kMaxE1; i += blockDim.x) (&cnt[0][0])[i] = 0;
   __syncthreads();
   count_chunk<kPer>(ev, start, end, cnt[wv]);
