@@ -118,6 +118,58 @@ def cpu_baseline(inp, budget_s: float):
                       f"oracle, median of {len(times)} runs ({med:.2f} s each)"}
 
 
+def fusion_ab(cfg, bm, x, logits, weights, fused, steps):
+    """The pages' comparison: the layer with the shared-experts fusion (one top-(K+1) pass) and
+    without it (a top-K routed pass plus a separate shared pass, added in the combine), same
+    kernels. Each flow is captured as HIP graphs (one per weight set) and replayed alternately,
+    so host launch overhead is out of the timing."""
+    import torch
+    from shared_routed_expert_amd import UnfusedMoE
+    unf = UnfusedMoE(cfg.T, cfg.H, cfg.I, cfg.E, cfg.K, bm, weights[0].scale_mode, device="cuda")
+    flows = {
+        "fused_one_call": lambda W, s: fused.forward_fused(x, logits, W, 1.0, s),
+        "fused_four_calls": lambda W, s: fused.forward(x, logits, W, 1.0, s),
+        "unfused": lambda W, s: unf.forward(x, logits, W, 1.0, s),
+        "unfused_split_shared": lambda W, s: unf.forward(x, logits, W, 1.0, s, shared_split=True),
+    }
+    side = torch.cuda.Stream()
+    res = {}
+    timing = "graph replay, weight sets alternated"
+    for name, fn in flows.items():
+        with torch.cuda.stream(side):
+            for W in weights:
+                fn(W, side)   # warm-up and one-time setup outside the capture
+        torch.cuda.synchronize()
+        try:
+            graphs = []
+            for W in weights:
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=side):
+                    fn(W, side)
+                graphs.append(g)
+            run = lambda i: graphs[i % len(graphs)].replay()
+        except Exception as exc:  # pragma: no cover - capture not available
+            log(f"bench: graph capture failed for {name} ({exc}); timing eager launches")
+            timing = "eager launches (graph capture failed)"
+            run = lambda i: fn(weights[i % len(weights)], side)
+        for i in range(4):
+            run(i)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(side)
+        for i in range(steps):
+            with torch.cuda.stream(side):
+                run(i)
+        e1.record(side)
+        torch.cuda.synchronize()
+        res[name + "_us"] = round(1e3 * e0.elapsed_time(e1) / steps, 2)
+    # the unfused baseline at its best: the shared pass on whichever kernels run it faster
+    res["unfused_best_us"] = min(res["unfused_us"], res["unfused_split_shared_us"])
+    res["unfused_over_fused"] = round(res["unfused_best_us"] / res["fused_one_call_us"], 4)
+    res["timing"] = timing
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -128,6 +180,7 @@ def main():
     ap.add_argument("--weight-sets", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=30.0)
+    ap.add_argument("--no-fusion-ab", action="store_true", help="skip the fused-vs-unfused comparison")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
                     help="only run a plain copy of this many MiB (counter calibration) and exit")
     args = ap.parse_args()
@@ -265,6 +318,9 @@ def main():
                   "entry_point": "moe_layer_forward",
                   "four_call_ms_per_step": round(four_ms, 5)},
     }
+    if not args.no_fusion_ab:
+        log("bench: fused vs unfused layer (graph replays)")
+        result["fusion_ab"] = fusion_ab(cfg, bm, x, logits, weights, layer, args.steps)
     if not args.no_cpu_baseline:
         log("bench: timing the CPU oracle")
         result["cpu_baseline"] = cpu_baseline(inp, args.cpu_budget)

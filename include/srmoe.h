@@ -77,6 +77,31 @@ int moe_route_topk_plus_shared(const float* logits, int T, int E, int K, float s
                                int32_t* topk_ids, float* topk_w, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * The unfused layer, for the fused-vs-unfused comparison: the routed experts and
+ * the shared expert computed as two passes and added (the pages' formulation
+ * before the fusion: intelliparadigm section 2.1, shared output plus the weighted
+ * routed outputs).
+ *
+ * moe_route_topk: step 1 without the shared slot -- the same top-K, order and
+ * weights, rows of K entries.   topk_ids / topk_w [T,K] out; limits 1 <= K <=
+ * min(E,15), E <= 256.
+ *
+ * The routed pass is then moe_align_by_expert + moe_fused_ffn with K1 = K, E1 = E
+ * (the first E experts of w13/s13/w2/s2); the shared pass is moe_fused_ffn with
+ * K1 = 1, E1 = 1 (the shared expert's weights; every token routed to it with
+ * weight shared_weight, a layout that does not depend on the routing).
+ *
+ * moe_combine_unfused: out[t,:] = bf16( sum_{k<K} routed[t,k,:] + shared[t,:] ),
+ * accumulated in float32 in that order -- the order of moe_combine over the fused
+ * K+1 slots, so the two layers agree bit for bit. routed_ws / shared_ws are the
+ * workspaces of the two passes (>= T*K*H*2 and T*H*2 bytes of slot rows).
+ * ------------------------------------------------------------------------- */
+int moe_route_topk(const float* logits, int T, int E, int K, int32_t* topk_ids, float* topk_w,
+                   void* stream);
+int moe_combine_unfused(int T, int K, int H, const void* routed_ws, size_t routed_ws_bytes,
+                        const void* shared_ws, size_t shared_ws_bytes, uint16_t* out, void* stream);
+
+/* ---------------------------------------------------------------------------
  * Step 2: align / sort / pad the T*(K+1) (token, slot) entries by expert.
  * Entry s = t*K1 + k has expert topk_ids[s]. Output, for experts in ascending
  * id, the entries of each expert in ascending s (a stable counting sort),

@@ -41,6 +41,8 @@ def _load():
         "moe_ffn_experts": ([P, P, P, P, I, I, I, I, I, I, I, P, P, P, P, P, Z, P], I),
         "moe_ffn_experts_one_kernel": ([I, I, I], I),
         "moe_combine": ([I, I, I, P, Z, P, P], I),
+        "moe_route_topk": ([P, I, I, I, P, P, P], I),
+        "moe_combine_unfused": ([I, I, I, P, Z, P, Z, P, P], I),
         "moe_layer_forward": ([P, P, P, P, P, P, I, I, I, I, I, I, F, I, P, P, P, P, P, P, P, P, Z, P, Z, P, P], I),
         "moe_sorted_capacity": ([I, I, I, I], Z),
         "moe_align_workspace_bytes": ([I, I, I], Z),
@@ -60,7 +62,7 @@ lib = _load()
 
 EXPORTED = ("moe_route_topk_plus_shared", "moe_align_by_expert", "moe_fused_ffn", "moe_ffn_quant_x",
             "moe_ffn_gate_up", "moe_ffn_down", "moe_ffn_experts", "moe_ffn_experts_one_kernel",
-            "moe_combine", "moe_layer_forward", "moe_sorted_capacity",
+            "moe_combine", "moe_layer_forward", "moe_route_topk", "moe_combine_unfused", "moe_sorted_capacity",
             "moe_align_workspace_bytes", "moe_ffn_workspace_bytes", "moe_ffn_workspace_offsets",
             "srmoe_status_string",
             "srmoe_last_hip_error")
@@ -169,6 +171,18 @@ def moe_ffn_experts_one_kernel(H, I, block_m):
 def moe_combine(T, K1, H, workspace, ws_bytes, out, stream=None, check=True):
     st = lib.moe_combine(T, K1, H, _ptr(workspace), ws_bytes, _ptr(out), _stream(stream))
     return _check("moe_combine", st) if check else st
+
+
+def moe_route_topk(logits, T, E, K, topk_ids, topk_w, stream=None, check=True):
+    st = lib.moe_route_topk(_ptr(logits), T, E, K, _ptr(topk_ids), _ptr(topk_w), _stream(stream))
+    return _check("moe_route_topk", st) if check else st
+
+
+def moe_combine_unfused(T, K, H, routed_ws, routed_ws_bytes, shared_ws, shared_ws_bytes, out, stream=None,
+                        check=True):
+    st = lib.moe_combine_unfused(T, K, H, _ptr(routed_ws), routed_ws_bytes, _ptr(shared_ws), shared_ws_bytes,
+                                 _ptr(out), _stream(stream))
+    return _check("moe_combine_unfused", st) if check else st
 
 
 def moe_layer_forward(x, logits, w13, s13, w2, s2, scale_mode, T, H, I, E, K, shared_weight, block_m,

@@ -6,6 +6,7 @@
 
 namespace srmoe {
 hipError_t launch_route(const float*, int, int, int, float, int32_t*, float*, hipStream_t);
+hipError_t launch_route_topk(const float*, int, int, int, int32_t*, float*, hipStream_t);
 size_t align_workspace_bytes(int T, int K1, int E1);
 hipError_t launch_align(const int32_t*, int, int, int, int, int32_t*, int32_t*, int32_t*, int32_t*,
                         int32_t*, void*, hipStream_t);
@@ -18,7 +19,7 @@ hipError_t launch_gate_up(const uint8_t*, const float*, const uint8_t*, const fl
 hipError_t launch_down(const uint8_t*, const float*, const uint8_t*, const float*, bool,
                        const int32_t*, const int32_t*, const int32_t*, const float*, uint16_t*, int,
                        int, int, int, int, int, hipStream_t);
-hipError_t launch_combine(const uint16_t*, int, int, int, uint16_t*, hipStream_t);
+hipError_t launch_combine(const uint16_t*, const uint16_t*, int, int, int, uint16_t*, hipStream_t);
 hipError_t launch_gate_up_decode(const uint8_t*, const float*, const uint8_t*, const float*, bool,
                                  const int32_t*, const int32_t*, float*, int, int, int, int, int,
                                  hipStream_t);
@@ -150,6 +151,16 @@ int moe_route_topk_plus_shared(const float* logits, int T, int E, int K, float s
   if (!logits || !topk_ids || !topk_w) return SRMOE_ERR_INVALID_ARG;
   if (!aligned16(logits) || !aligned16(topk_ids) || !aligned16(topk_w)) return SRMOE_ERR_INVALID_ARG;
   return hip_status(launch_route(logits, T, E, K, shared_weight, topk_ids, topk_w, as_stream(stream)));
+}
+
+int moe_route_topk(const float* logits, int T, int E, int K, int32_t* topk_ids, float* topk_w,
+                   void* stream) {
+  if (T < 0 || T > kMaxT || E < 1 || K < 1) return SRMOE_ERR_INVALID_ARG;
+  if (E > 256 || K > E || K > 15) return SRMOE_ERR_UNSUPPORTED;
+  if (T == 0) return SRMOE_OK;
+  if (!logits || !topk_ids || !topk_w) return SRMOE_ERR_INVALID_ARG;
+  if (!aligned16(logits) || !aligned16(topk_ids) || !aligned16(topk_w)) return SRMOE_ERR_INVALID_ARG;
+  return hip_status(launch_route_topk(logits, T, E, K, topk_ids, topk_w, as_stream(stream)));
 }
 
 int moe_align_by_expert(const int32_t* topk_ids, int T, int K1, int E1, int block_m,
@@ -362,7 +373,22 @@ int moe_combine(int T, int K1, int H, const void* workspace, size_t ws_bytes, ui
   if (T == 0) return SRMOE_OK;
   if (!workspace || !out || !aligned16(workspace) || !aligned16(out)) return SRMOE_ERR_INVALID_ARG;
   if (ws_bytes < (size_t)T * K1 * H * 2) return SRMOE_ERR_WORKSPACE;
-  return hip_status(launch_combine(static_cast<const uint16_t*>(workspace), T, K1, H, out,
+  return hip_status(launch_combine(static_cast<const uint16_t*>(workspace), nullptr, T, K1, H, out,
+                                   as_stream(stream)));
+}
+
+int moe_combine_unfused(int T, int K, int H, const void* routed_ws, size_t routed_ws_bytes,
+                        const void* shared_ws, size_t shared_ws_bytes, uint16_t* out, void* stream) {
+  if (T < 0 || T > kMaxT || K < 1 || H <= 0) return SRMOE_ERR_INVALID_ARG;
+  if (K > 16 || H % 128 != 0 || (size_t)T * K * H >= ((size_t)1 << 31)) return SRMOE_ERR_UNSUPPORTED;
+  if (T == 0) return SRMOE_OK;
+  if (!routed_ws || !shared_ws || !out || !aligned16(routed_ws) || !aligned16(shared_ws) ||
+      !aligned16(out))
+    return SRMOE_ERR_INVALID_ARG;
+  if (routed_ws_bytes < (size_t)T * K * H * 2 || shared_ws_bytes < (size_t)T * H * 2)
+    return SRMOE_ERR_WORKSPACE;
+  return hip_status(launch_combine(static_cast<const uint16_t*>(routed_ws),
+                                   static_cast<const uint16_t*>(shared_ws), T, K, H, out,
                                    as_stream(stream)));
 }
 

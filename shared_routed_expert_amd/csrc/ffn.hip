@@ -311,23 +311,27 @@ hipError_t launch_down(const uint8_t* aq, const float* sa, const uint8_t* w2, co
                : launch_down_t<false>(block_m, grid, stream, aq, sa, w2, s2, sorted, block_expert, row_scale, slot_out, T, H, I, K1);
 }
 
-// out[t, :] = bf16( sum_k slot_out[t*K1 + k, :] ), float32 in slot order. 8 columns per thread.
-// K1 is a template parameter so that all K1 row loads are issued before the first add
-// (with a runtime trip count they go out one at a time, each waiting for memory).
-template <int K1>
-__global__ void __launch_bounds__(256) combine_kernel(const uint16_t* __restrict__ slot_out, int T,
+// out[t, :] = bf16( sum_k slot_out[t*K1 + k, :] (+ extra[t, :]) ), float32 in slot order,
+// extra (the separately computed shared expert of the unfused layer, or null) last.
+// 8 columns per thread. K1 is a template parameter so that all K1 row loads are issued
+// before the first add (with a runtime trip count they go out one at a time, each
+// waiting for memory).
+template <int K1, bool kExtra>
+__global__ void __launch_bounds__(256) combine_kernel(const uint16_t* __restrict__ slot_out,
+                                                      const uint16_t* __restrict__ extra, int T,
                                                       int H, uint16_t* __restrict__ out) {
   const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
   const int n8 = H / 8;
   const size_t t = idx / n8;
   if (t >= (size_t)T) return;
   const int h = (int)(idx % n8) * 8;
-  uint4 v[K1];
+  uint4 v[K1 + 1];
 #pragma unroll
   for (int k = 0; k < K1; ++k) v[k] = *reinterpret_cast<const uint4*>(slot_out + (t * K1 + k) * H + h);
+  if (kExtra) v[K1] = *reinterpret_cast<const uint4*>(extra + t * H + h);
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int k = 0; k < K1; ++k) {
+  for (int k = 0; k < K1 + (kExtra ? 1 : 0); ++k) {
     const uint32_t w[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -343,14 +347,17 @@ __global__ void __launch_bounds__(256) combine_kernel(const uint16_t* __restrict
   *reinterpret_cast<uint4*>(out + t * H + h) = o;
 }
 
-hipError_t launch_combine(const uint16_t* slot_out, int T, int K1, int H, uint16_t* out,
-                          hipStream_t stream) {
+hipError_t launch_combine(const uint16_t* slot_out, const uint16_t* extra, int T, int K1, int H,
+                          uint16_t* out, hipStream_t stream) {
   const size_t n = (size_t)T * (H / 8);
   const dim3 grid((unsigned)((n + 255) / 256)), blk(256);
   switch (K1) {
-#define SRMOE_COMBINE(K)                                                                  \
-    case K:                                                                               \
-      hipLaunchKernelGGL(combine_kernel<K>, grid, blk, 0, stream, slot_out, T, H, out); \
+#define SRMOE_COMBINE(K)                                                                             \
+    case K:                                                                                          \
+      if (extra)                                                                                     \
+        hipLaunchKernelGGL((combine_kernel<K, true>), grid, blk, 0, stream, slot_out, extra, T, H, out); \
+      else                                                                                           \
+        hipLaunchKernelGGL((combine_kernel<K, false>), grid, blk, 0, stream, slot_out, extra, T, H, out); \
       break;
     SRMOE_COMBINE(1) SRMOE_COMBINE(2) SRMOE_COMBINE(3) SRMOE_COMBINE(4) SRMOE_COMBINE(5)
     SRMOE_COMBINE(6) SRMOE_COMBINE(7) SRMOE_COMBINE(8) SRMOE_COMBINE(9) SRMOE_COMBINE(10)

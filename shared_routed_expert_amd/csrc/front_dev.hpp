@@ -23,12 +23,14 @@ __device__ __forceinline__ float key_to_float(uint32_t k) {
 // coefficient shared_weight. Each lane holds the logits of experts lane, lane+64,
 // ... (E <= 255); each of the K rounds is a local max and a DPP wave reduction of a
 // 64-bit key (ordered logit, 255 - id). ids/w are written to global memory;
-// lds_ids (if not null) gets a copy of the ids.
+// lds_ids (if not null) gets a copy of the ids. With append_shared false the rows
+// have K entries and no shared slot (the routed-only router of the unfused layer).
 __device__ __forceinline__ void route_token_wave(const float* __restrict__ logits, int t, int E, int K,
                                                  float shared_weight, int32_t* __restrict__ ids,
-                                                 float* __restrict__ w, int* lds_ids) {
+                                                 float* __restrict__ w, int* lds_ids,
+                                                 bool append_shared = true) {
   const int lane = threadIdx.x & 63;
-  const int K1 = K + 1;
+  const int K1 = K + (append_shared ? 1 : 0);
   uint64_t key[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
@@ -75,7 +77,7 @@ __device__ __forceinline__ void route_token_wave(const float* __restrict__ logit
       if (lds_ids) lds_ids[t * K1 + k] = sel_id[k];
     }
   }
-  if (lane == K) {
+  if (append_shared && lane == K) {
     ids[(size_t)t * K1 + K] = E;
     w[(size_t)t * K1 + K] = shared_weight;
     if (lds_ids) lds_ids[t * K1 + K] = E;

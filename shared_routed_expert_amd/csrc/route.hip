@@ -17,10 +17,26 @@ __global__ void __launch_bounds__(256) route_topk_plus_shared_kernel(
   route_token_wave(logits, t, E, K, shared_weight, ids, w, nullptr);
 }
 
+// The routed-only router of the unfused layer (the shared expert computed apart, as in
+// the pages' unfused formulation): K entries per token, no shared slot.
+__global__ void __launch_bounds__(256) route_topk_kernel(const float* __restrict__ logits, int T,
+                                                         int E, int K, int32_t* __restrict__ ids,
+                                                         float* __restrict__ w) {
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  route_token_wave(logits, t, E, K, 0.f, ids, w, nullptr, false);
+}
+
 hipError_t launch_route(const float* logits, int T, int E, int K, float shared_weight, int32_t* ids,
                         float* w, hipStream_t stream) {
   hipLaunchKernelGGL(route_topk_plus_shared_kernel, dim3((T + 3) / 4), dim3(256), 0, stream, logits,
                      T, E, K, shared_weight, ids, w);
+  return hipGetLastError();
+}
+
+hipError_t launch_route_topk(const float* logits, int T, int E, int K, int32_t* ids, float* w,
+                             hipStream_t stream) {
+  hipLaunchKernelGGL(route_topk_kernel, dim3((T + 3) / 4), dim3(256), 0, stream, logits, T, E, K, ids, w);
   return hipGetLastError();
 }
 

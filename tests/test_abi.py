@@ -179,6 +179,30 @@ def test_ffn_experts_one_kernel_shapes(L):
     assert not one(5248, 192, 16) and not one(5120, 32, 16)
 
 
+def test_route_topk_rejects(L):
+    f = lambda *a: L.moe_route_topk(*a, stream=0, check=False)
+    assert f(FAKE, -1, 160, 8, FAKE, FAKE) == -1
+    assert f(FAKE, 64, 160, 0, FAKE, FAKE) == -1
+    assert f(FAKE, 64, 160, 16, FAKE, FAKE) == -2 and f(FAKE, 64, 4, 5, FAKE, FAKE) == -2
+    assert f(FAKE, 64, 257, 8, FAKE, FAKE) == -2
+    assert f(None, 64, 160, 8, FAKE, FAKE) == -1 and f(FAKE, 64, 160, 8, MIS, FAKE) == -1
+    assert f(None, 0, 160, 8, None, None) == 0
+
+
+def test_combine_unfused_rejects(L):
+    f = lambda *a: L.moe_combine_unfused(*a, stream=0, check=False)
+    need_r, need_s = 64 * 8 * 5120 * 2, 64 * 5120 * 2
+    assert f(-1, 8, 5120, FAKE, need_r, FAKE, need_s, FAKE) == -1
+    assert f(64, 0, 5120, FAKE, need_r, FAKE, need_s, FAKE) == -1
+    assert f(64, 17, 5120, FAKE, need_r, FAKE, need_s, FAKE) == -2
+    assert f(64, 8, 5000, FAKE, need_r, FAKE, need_s, FAKE) == -2
+    assert f(64, 8, 5120, None, need_r, FAKE, need_s, FAKE) == -1
+    assert f(64, 8, 5120, FAKE, need_r, MIS, need_s, FAKE) == -1
+    assert f(64, 8, 5120, FAKE, need_r - 1, FAKE, need_s, FAKE) == -3
+    assert f(64, 8, 5120, FAKE, need_r, FAKE, need_s - 1, FAKE) == -3
+    assert f(0, 8, 5120, None, 0, None, 0, None) == 0
+
+
 def test_combine_rejects(L):
     f = lambda *a: L.moe_combine(*a, stream=0, check=False)
     assert f(-1, 9, 5120, FAKE, 1 << 30, FAKE) == -1

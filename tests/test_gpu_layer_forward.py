@@ -36,6 +36,10 @@ def _outputs(layer):
     # blocks per expert), and I = 256
     (small_cfg("decode_multigroup", T=64, H=256, I=128, E=4, K=2, seed=24), 16),
     (small_cfg("decode_i256", T=40, H=512, I=256, E=10, K=4, seed=25), 16),
+    # the in-kernel align of the one-kernel expert FFN: at its limit (4095 entries, 16-row
+    # blocks, many blocks per expert) and just past it (4104: the separate align runs)
+    (small_cfg("fold_align_max", T=455, H=256, I=64, E=40, K=8, seed=27), 16),
+    (small_cfg("fold_align_over", T=456, H=256, I=64, E=40, K=8, seed=28), 16),
 ])
 def test_layer_forward_matches_four_calls(cfg, bm):
     inp = generate(cfg)
