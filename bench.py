@@ -118,11 +118,62 @@ def cpu_baseline(inp, budget_s: float):
                       f"oracle, median of {len(times)} runs ({med:.2f} s each)"}
 
 
+def router_timing(inp, x, steps):
+    """The router gate upstream of the layer (moe_router_logits), timed on graph replays:
+    duration, float32-equivalent TFLOP/s and the bytes of x and the router weight."""
+    import torch
+    from shared_routed_expert_amd import _lib as L
+    c = inp.cfg
+    w = torch.from_numpy(inp.router_w).cuda()
+    bias = torch.from_numpy(inp.bias).cuda()
+    out = torch.empty((c.T, c.E), dtype=torch.float32, device="cuda")
+    wsb = L.moe_router_workspace_bytes(c.T, c.H, c.E)
+    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+    side = torch.cuda.Stream()
+    fn = lambda: L.moe_router_logits(x, w, bias, c.T, c.H, c.E, out, ws, wsb, side)
+    us = graph_time([fn], side, steps)
+    flops = 2.0 * c.T * c.H * c.E
+    nbytes = c.T * c.H * 2 + c.E * c.H * 4 + c.T * c.E * 4
+    return {"us": round(us, 2), "tflops_fp32_equiv": round(flops / us / 1e6, 2), "GBps": round(nbytes / us / 1e3, 1),
+            "bytes": nbytes, "timing": "graph replay"}
+
+
+GRAPH_ROUNDS = 8   # captured rounds per graph, so that the host's launch of a replay is amortised
+
+
+def graph_time(fns, stream, steps):
+    """Average GPU duration (us) of one call of the step functions in `fns` (called in turn,
+    e.g. one per weight set): GRAPH_ROUNDS rounds of them are captured as one HIP graph,
+    which is replayed until about `steps` calls have run."""
+    import torch
+    with torch.cuda.stream(stream):
+        for fn in fns:
+            fn()   # warm-up and one-time setup outside the capture
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        for _ in range(GRAPH_ROUNDS):
+            for fn in fns:
+                fn()
+    per_replay = GRAPH_ROUNDS * len(fns)
+    replays = max(1, steps // per_replay)
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        e0.record(stream)
+        for _ in range(replays):
+            g.replay()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    return 1e3 * e0.elapsed_time(e1) / (replays * per_replay)
+
+
 def fusion_ab(cfg, bm, x, logits, weights, fused, steps):
     """The pages' comparison: the layer with the shared-experts fusion (one top-(K+1) pass) and
     without it (a top-K routed pass plus a separate shared pass, added in the combine), same
-    kernels. Each flow is captured as HIP graphs (one per weight set) and replayed alternately,
-    so host launch overhead is out of the timing."""
+    kernels. Each flow is captured as a HIP graph of several steps over the weight sets in
+    turn and replayed, so host launch overhead is out of the timing."""
     import torch
     from shared_routed_expert_amd import UnfusedMoE
     unf = UnfusedMoE(cfg.T, cfg.H, cfg.I, cfg.E, cfg.K, bm, weights[0].scale_mode, device="cuda")
@@ -134,35 +185,23 @@ def fusion_ab(cfg, bm, x, logits, weights, fused, steps):
     }
     side = torch.cuda.Stream()
     res = {}
-    timing = "graph replay, weight sets alternated"
+    timing = f"graph replay ({GRAPH_ROUNDS} rounds of the weight sets per graph)"
     for name, fn in flows.items():
-        with torch.cuda.stream(side):
-            for W in weights:
-                fn(W, side)   # warm-up and one-time setup outside the capture
-        torch.cuda.synchronize()
+        steps_fns = [lambda W=W, fn=fn: fn(W, side) for W in weights]
         try:
-            graphs = []
-            for W in weights:
-                g = torch.cuda.CUDAGraph()
-                with torch.cuda.graph(g, stream=side):
-                    fn(W, side)
-                graphs.append(g)
-            run = lambda i: graphs[i % len(graphs)].replay()
+            us = graph_time(steps_fns, side, steps)
         except Exception as exc:  # pragma: no cover - capture not available
             log(f"bench: graph capture failed for {name} ({exc}); timing eager launches")
             timing = "eager launches (graph capture failed)"
-            run = lambda i: fn(weights[i % len(weights)], side)
-        for i in range(4):
-            run(i)
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(side)
-        for i in range(steps):
-            with torch.cuda.stream(side):
-                run(i)
-        e1.record(side)
-        torch.cuda.synchronize()
-        res[name + "_us"] = round(1e3 * e0.elapsed_time(e1) / steps, 2)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            e0.record(side)
+            for i in range(steps):
+                steps_fns[i % len(steps_fns)]()
+            e1.record(side)
+            torch.cuda.synchronize()
+            us = 1e3 * e0.elapsed_time(e1) / steps
+        res[name + "_us"] = round(us, 2)
     # the unfused baseline at its best: the shared pass on whichever kernels run it faster
     res["unfused_best_us"] = min(res["unfused_us"], res["unfused_split_shared_us"])
     res["unfused_over_fused"] = round(res["unfused_best_us"] / res["fused_one_call_us"], 4)
@@ -318,6 +357,8 @@ def main():
                   "entry_point": "moe_layer_forward",
                   "four_call_ms_per_step": round(four_ms, 5)},
     }
+    log("bench: router gate (graph replays)")
+    result["router_gate"] = router_timing(inp, x, args.steps)
     if not args.no_fusion_ab:
         log("bench: fused vs unfused layer (graph replays)")
         result["fusion_ab"] = fusion_ab(cfg, bm, x, logits, weights, layer, args.steps)

@@ -77,6 +77,22 @@ int moe_route_topk_plus_shared(const float* logits, int T, int E, int K, float s
                                int32_t* topk_ids, float* topk_w, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * The router gate, upstream of step 1 (each token scores the E routed experts;
+ * Novita AI section 1): logits[t,e] = sum_h x[t,h] * w_router[e,h] + bias[e].
+ *   x [T,H] bf16; w_router [E,H] float32; bias [E] float32 or NULL; logits [T,E]
+ *   float32 out (the input of moe_route_topk_plus_shared).
+ *   Float32-accurate on the bf16 matrix cores: each weight is split into three bf16
+ *   parts that carry its 24 significand bits, so every product with the bf16 x is
+ *   exact and the sums are float32. Deterministic (K-split partials are summed in a
+ *   fixed order).
+ *   workspace >= moe_router_workspace_bytes(T,H,E) bytes (those partials), device.
+ *   limits: H % 128 == 0, 1 <= E <= 256.
+ * ------------------------------------------------------------------------- */
+int moe_router_logits(const uint16_t* x, const float* w_router, const float* bias, int T, int H, int E,
+                      float* logits, void* workspace, size_t ws_bytes, void* stream);
+size_t moe_router_workspace_bytes(int T, int H, int E); /* host */
+
+/* ---------------------------------------------------------------------------
  * The unfused layer, for the fused-vs-unfused comparison: the routed experts and
  * the shared expert computed as two passes and added (the pages' formulation
  * before the fusion: intelliparadigm section 2.1, shared output plus the weighted

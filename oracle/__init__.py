@@ -32,11 +32,11 @@ something other than itself -- brute force on tiny inputs, library routines
 own fused == unfused check. No function here is "parity unpinned".
 """
 from .fp8 import e4m3_decode, e4m3_encode, E4M3_MAX
-from .moe import (route_topk, route_topk_plus_shared, align_by_expert, sorted_capacity,
+from .moe import (router_logits, route_topk, route_topk_plus_shared, align_by_expert, sorted_capacity,
                   quantize_act, dequant_weight, expert_ffn, moe_unfused, moe_fused,
                   slot_outputs, combine_slots, dense_shared_ffn)
 
-__all__ = ["e4m3_decode", "e4m3_encode", "E4M3_MAX", "route_topk", "route_topk_plus_shared",
+__all__ = ["e4m3_decode", "e4m3_encode", "E4M3_MAX", "router_logits", "route_topk", "route_topk_plus_shared",
            "align_by_expert", "sorted_capacity", "quantize_act", "dequant_weight",
            "expert_ffn", "moe_unfused", "moe_fused", "slot_outputs", "combine_slots",
            "dense_shared_ffn"]

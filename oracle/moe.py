@@ -36,6 +36,21 @@ from .fp8 import e4m3_decode, e4m3_encode, E4M3_MAX
 GROUP = 128
 
 
+# ----------------------------------------------------------------------------- router gate
+def router_logits(x_f32: np.ndarray, router_w: np.ndarray, bias: np.ndarray | None = None) -> np.ndarray:
+    """The router gate upstream of the routing: logits[t, e] = sum_h x[t, h] * W_r[e, h]
+    (+ bias[e]) for the E routed experts, in float64. Each token scores the 160 routed
+    experts and keeps its top-8 (Optimizing GLM4-MoE for production, section 1); the
+    gate itself is the plain linear router over the hidden state.
+
+    x_f32 [T, H], router_w [E, H], bias [E] or None. Returns float64 [T, E].
+    """
+    lg = np.asarray(x_f32, np.float64) @ np.asarray(router_w, np.float64).T
+    if bias is not None:
+        lg = lg + np.asarray(bias, np.float64)[None, :]
+    return lg
+
+
 # ----------------------------------------------------------------------------- routing
 def route_topk(logits: np.ndarray, K: int):
     """Top-K routed experts per token, ordered by (logit desc, id asc), with weights

@@ -42,6 +42,8 @@ def _load():
         "moe_ffn_experts_one_kernel": ([I, I, I], I),
         "moe_combine": ([I, I, I, P, Z, P, P], I),
         "moe_route_topk": ([P, I, I, I, P, P, P], I),
+        "moe_router_logits": ([P, P, P, I, I, I, P, P, Z, P], I),
+        "moe_router_workspace_bytes": ([I, I, I], Z),
         "moe_combine_unfused": ([I, I, I, P, Z, P, Z, P, P], I),
         "moe_layer_forward": ([P, P, P, P, P, P, I, I, I, I, I, I, F, I, P, P, P, P, P, P, P, P, Z, P, Z, P, P], I),
         "moe_sorted_capacity": ([I, I, I, I], Z),
@@ -62,7 +64,8 @@ lib = _load()
 
 EXPORTED = ("moe_route_topk_plus_shared", "moe_align_by_expert", "moe_fused_ffn", "moe_ffn_quant_x",
             "moe_ffn_gate_up", "moe_ffn_down", "moe_ffn_experts", "moe_ffn_experts_one_kernel",
-            "moe_combine", "moe_layer_forward", "moe_route_topk", "moe_combine_unfused", "moe_sorted_capacity",
+            "moe_combine", "moe_layer_forward", "moe_route_topk", "moe_combine_unfused", "moe_router_logits",
+            "moe_router_workspace_bytes", "moe_sorted_capacity",
             "moe_align_workspace_bytes", "moe_ffn_workspace_bytes", "moe_ffn_workspace_offsets",
             "srmoe_status_string",
             "srmoe_last_hip_error")
@@ -171,6 +174,16 @@ def moe_ffn_experts_one_kernel(H, I, block_m):
 def moe_combine(T, K1, H, workspace, ws_bytes, out, stream=None, check=True):
     st = lib.moe_combine(T, K1, H, _ptr(workspace), ws_bytes, _ptr(out), _stream(stream))
     return _check("moe_combine", st) if check else st
+
+
+def moe_router_workspace_bytes(T, H, E):
+    return lib.moe_router_workspace_bytes(T, H, E)
+
+
+def moe_router_logits(x, w_router, bias, T, H, E, logits, workspace, ws_bytes, stream=None, check=True):
+    st = lib.moe_router_logits(_ptr(x), _ptr(w_router), _ptr(bias), T, H, E, _ptr(logits), _ptr(workspace),
+                               ws_bytes, _stream(stream))
+    return _check("moe_router_logits", st) if check else st
 
 
 def moe_route_topk(logits, T, E, K, topk_ids, topk_w, stream=None, check=True):

@@ -7,6 +7,9 @@
 namespace srmoe {
 hipError_t launch_route(const float*, int, int, int, float, int32_t*, float*, hipStream_t);
 hipError_t launch_route_topk(const float*, int, int, int, int32_t*, float*, hipStream_t);
+size_t router_workspace_bytes(int T, int H, int E);
+hipError_t launch_router(const uint16_t*, const float*, const float*, int, int, int, float*, float*,
+                         hipStream_t);
 size_t align_workspace_bytes(int T, int K1, int E1);
 hipError_t launch_align(const int32_t*, int, int, int, int, int32_t*, int32_t*, int32_t*, int32_t*,
                         int32_t*, void*, hipStream_t);
@@ -151,6 +154,26 @@ int moe_route_topk_plus_shared(const float* logits, int T, int E, int K, float s
   if (!logits || !topk_ids || !topk_w) return SRMOE_ERR_INVALID_ARG;
   if (!aligned16(logits) || !aligned16(topk_ids) || !aligned16(topk_w)) return SRMOE_ERR_INVALID_ARG;
   return hip_status(launch_route(logits, T, E, K, shared_weight, topk_ids, topk_w, as_stream(stream)));
+}
+
+size_t moe_router_workspace_bytes(int T, int H, int E) {
+  if (T < 0 || H <= 0 || E < 1) return 0;
+  const size_t n = router_workspace_bytes(T, H, E);
+  return n > 256 ? n : 256;
+}
+
+int moe_router_logits(const uint16_t* x, const float* w_router, const float* bias, int T, int H, int E,
+                      float* logits, void* workspace, size_t ws_bytes, void* stream) {
+  if (T < 0 || T > kMaxT || H <= 0 || E < 1) return SRMOE_ERR_INVALID_ARG;
+  if (H % 128 != 0 || E > 256) return SRMOE_ERR_UNSUPPORTED;
+  if (T == 0) return SRMOE_OK;
+  if (!x || !w_router || !logits || !workspace) return SRMOE_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(w_router) || !aligned16(logits) || !aligned16(workspace) ||
+      (bias && !aligned16(bias)))
+    return SRMOE_ERR_INVALID_ARG;
+  if (ws_bytes < moe_router_workspace_bytes(T, H, E)) return SRMOE_ERR_WORKSPACE;
+  return hip_status(launch_router(x, w_router, bias, T, H, E, logits, static_cast<float*>(workspace),
+                                  as_stream(stream)));
 }
 
 int moe_route_topk(const float* logits, int T, int E, int K, int32_t* topk_ids, float* topk_w,

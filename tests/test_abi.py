@@ -179,6 +179,23 @@ def test_ffn_experts_one_kernel_shapes(L):
     assert not one(5248, 192, 16) and not one(5120, 32, 16)
 
 
+def test_router_logits_rejects(L):
+    f = lambda **kw: L.moe_router_logits(**{**dict(x=FAKE, w_router=FAKE, bias=None, T=64, H=5120, E=160,
+                                                    logits=FAKE, workspace=FAKE, ws_bytes=1 << 30), **kw},
+                                         stream=0, check=False)
+    assert f(T=-1) == -1 and f(H=0) == -1 and f(E=0) == -1
+    assert f(H=5000) == -2 and f(E=257) == -2
+    for name in ("x", "w_router", "logits", "workspace"):
+        assert f(**{name: None}) == -1, name
+        assert f(**{name: MIS}) == -1, name
+    assert f(bias=MIS) == -1
+    assert f(ws_bytes=L.moe_router_workspace_bytes(64, 5120, 160) - 1) == -3
+    assert f(T=0, x=None) == 0
+    # batches too small to fill the GPU with tiles split K (partials in the workspace)
+    assert L.moe_router_workspace_bytes(64, 5120, 160) > 64 * 160 * 4
+    assert L.moe_router_workspace_bytes(4096, 5120, 160) >= 256
+
+
 def test_route_topk_rejects(L):
     f = lambda *a: L.moe_route_topk(*a, stream=0, check=False)
     assert f(FAKE, -1, 160, 8, FAKE, FAKE) == -1

@@ -199,3 +199,40 @@ def test_fp32_masters_close_to_fp8(tiny):
                            tiny.s13, tiny.w2_q, tiny.s2)
     rel = np.max(np.abs(got - ref), axis=1) / np.max(np.abs(ref), axis=1)
     assert rel.max() < 0.15
+
+
+# ---------------------------------------------------------------------------- router gate
+def test_router_logits_bruteforce():
+    """Pure-Python triple loop on tiny inputs (no numpy matmul), bias included."""
+    rng = np.random.default_rng(5)
+    x = rng.standard_normal((3, 7)).astype(np.float32)
+    w = rng.standard_normal((4, 7)).astype(np.float32)
+    b = rng.standard_normal(4).astype(np.float32)
+    got = oracle.router_logits(x, w, b)
+    for t in range(3):
+        for e in range(4):
+            acc = float(b[e])
+            for h in range(7):
+                acc += float(x[t, h]) * float(w[e, h])
+            assert abs(got[t, e] - acc) <= 1e-12 * (1 + abs(acc))
+
+
+def test_router_logits_one_hot_rows():
+    """x = unit vectors: the logits are the router weight's columns (plus the bias), exactly."""
+    rng = np.random.default_rng(6)
+    w = rng.standard_normal((5, 8)).astype(np.float32)
+    b = rng.standard_normal(5).astype(np.float32)
+    got = oracle.router_logits(np.eye(8, dtype=np.float32), w, b)
+    assert np.array_equal(got, w.T.astype(np.float64) + b.astype(np.float64)[None, :])
+    assert np.array_equal(oracle.router_logits(np.eye(8, dtype=np.float32), w), w.T.astype(np.float64))
+
+
+@pytest.mark.parametrize("name", ["tiny", "prefill16k_zipf"])
+def test_router_logits_reproduce_the_workload_logits(name):
+    """The workloads' logits are the router gate of their x and router weight, rounded to fp32."""
+    cfg = CONFIGS[name]
+    if name != "tiny":
+        cfg = cfg.replace(T=64)
+    inp = generate(cfg)
+    lg = oracle.router_logits(f32_from_bf16_bits(inp.x_bf16), inp.router_w, inp.bias)
+    assert np.array_equal(lg.astype(np.float32), inp.logits)
