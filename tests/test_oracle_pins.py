@@ -236,3 +236,57 @@ def test_router_logits_reproduce_the_workload_logits(name):
     inp = generate(cfg)
     lg = oracle.router_logits(f32_from_bf16_bits(inp.x_bf16), inp.router_w, inp.bias)
     assert np.array_equal(lg.astype(np.float32), inp.logits)
+
+
+# ---------------------------------------------------------------------------- QK-Norm + half RoPE
+def test_head_rms_norm_closed_forms():
+    # a constant head c: every entry becomes sign(c) / sqrt(1 + eps / c^2) * w
+    w = np.linspace(0.5, 1.5, 8)
+    got = oracle.head_rms_norm(np.full((1, 8), -3.0), w, 1e-6)
+    assert np.allclose(got, -w / np.sqrt(1 + 1e-6 / 9.0), rtol=0, atol=1e-15)
+    # unit weight, eps 0: the result has mean square exactly 1 (up to rounding)
+    x = np.random.default_rng(1).standard_normal((5, 3, 16))
+    y = oracle.head_rms_norm(x, np.ones(16), 0.0)
+    assert np.allclose(np.mean(y * y, axis=-1), 1.0, atol=1e-14)
+    # scale invariance with eps = 0
+    assert np.allclose(oracle.head_rms_norm(7.5 * x, np.ones(16), 0.0), y, atol=1e-14)
+
+
+def test_rope_half_properties():
+    rng = np.random.default_rng(2)
+    x = rng.standard_normal((4, 2, 16))
+    rd = 8
+    # position 0 is the identity
+    a0 = oracle.rope_angles(np.zeros(4), rd, 10000.0)
+    assert np.array_equal(oracle.rope_half(x, a0, rd), x)
+    pos = np.array([1, 5, 17, 1000])
+    a = oracle.rope_angles(pos, rd, 10000.0)
+    y = oracle.rope_half(x, a, rd)
+    # the unrotated half passes through; each rotated pair keeps its length
+    assert np.array_equal(y[..., rd:], x[..., rd:])
+    h = rd // 2
+    assert np.allclose(y[..., :h] ** 2 + y[..., h:rd] ** 2, x[..., :h] ** 2 + x[..., h:rd] ** 2, atol=1e-12)
+    # rotations compose: rotate by p then by q == rotate by p + q
+    b = oracle.rope_angles(np.array([3, 4, 5, 6]), rd, 10000.0)
+    ab = oracle.rope_angles(pos + np.array([3, 4, 5, 6]), rd, 10000.0)
+    assert np.allclose(oracle.rope_half(y, b, rd), oracle.rope_half(x, ab, rd), atol=1e-10)
+    # pair 0 at position p is the complex product (x1 + i x2) * e^{i p} (theta^0 = 1)
+    z = (x[:, :, 0] + 1j * x[:, :, h]) * np.exp(1j * pos.astype(np.float64))[:, None]
+    assert np.allclose(y[:, :, 0], z.real, atol=1e-12) and np.allclose(y[:, :, h], z.imag, atol=1e-12)
+
+
+def test_qk_norm_rope_layout():
+    """q and k heads are normalised with their own weights and rotated; v passes through."""
+    rng = np.random.default_rng(3)
+    T, Hq, Hkv, D, rd = 3, 2, 1, 8, 4
+    qkv = rng.standard_normal((T, (Hq + 2 * Hkv) * D))
+    qw, kw = rng.uniform(0.5, 1.5, D), rng.uniform(0.5, 1.5, D)
+    pos = np.array([0, 2, 9])
+    out = oracle.qk_norm_rope(qkv, Hq, Hkv, D, rd, qw, kw, 1e-6, pos, 10000.0)
+    heads_in = qkv.reshape(T, Hq + 2 * Hkv, D)
+    heads = out.reshape(T, Hq + 2 * Hkv, D)
+    assert np.array_equal(heads[:, Hq + Hkv:], heads_in[:, Hq + Hkv:])            # v
+    assert np.allclose(heads[0, :Hq], oracle.head_rms_norm(heads_in[0, :Hq], qw, 1e-6))   # position 0: norm only
+    assert np.allclose(heads[0, Hq], oracle.head_rms_norm(heads_in[0, Hq], kw, 1e-6))
+    # dims past rotary_dim are the normalised values at every position
+    assert np.allclose(heads[:, :Hq, rd:], oracle.head_rms_norm(heads_in[:, :Hq], qw, 1e-6)[..., rd:])
