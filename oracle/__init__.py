@@ -36,9 +36,9 @@ from .moe import (router_logits, route_topk, route_topk_plus_shared, align_by_ex
                   quantize_act, dequant_weight, expert_ffn, moe_unfused, moe_fused,
                   slot_outputs, combine_slots, dense_shared_ffn)
 
-from .attn import qk_norm_rope, head_rms_norm, rope_half, rope_angles
+from .attn import qk_norm_rope, head_rms_norm, rope_half, rope_interleaved, rope_angles
 
-__all__ = ["qk_norm_rope", "head_rms_norm", "rope_half", "rope_angles", "e4m3_decode", "e4m3_encode", "E4M3_MAX", "router_logits", "route_topk", "route_topk_plus_shared",
+__all__ = ["qk_norm_rope", "head_rms_norm", "rope_half", "rope_interleaved", "rope_angles", "e4m3_decode", "e4m3_encode", "E4M3_MAX", "router_logits", "route_topk", "route_topk_plus_shared",
            "align_by_expert", "sorted_capacity", "quantize_act", "dequant_weight",
            "expert_ffn", "moe_unfused", "moe_fused", "slot_outputs", "combine_slots",
            "dense_shared_ffn"]

@@ -10,9 +10,11 @@ section 2). Readings of what they leave open:
 * Norm: RMS normalisation over the head dimension with a learned weight per
   dimension (separate weights for q and k), y = x / sqrt(mean(x^2) + eps) * w --
   the head norm of the Qwen-MoE models the pages name as the source.
-* Rotation: the first ``rotary_dim`` dimensions of each head are rotated in the
-  rotate-half pairing (dimension i with i + rotary_dim/2), the rest pass through;
-  angle(pos, i) = pos * theta^(-2i / rotary_dim).
+* Rotation: the first ``rotary_dim`` dimensions of each head are rotated, the rest
+  pass through; angle(pos, i) = pos * theta^(-2i / rotary_dim) for frequency i <
+  rotary_dim/2. The pages do not say how dimensions pair up, so both usual
+  arrangements are here: rotate-half (dimension i with i + rotary_dim/2, the default)
+  and interleaved (2i with 2i + 1).
 """
 from __future__ import annotations
 
@@ -47,18 +49,33 @@ def rope_half(x: np.ndarray, angle: np.ndarray, rotary_dim: int) -> np.ndarray:
     return out
 
 
+def rope_interleaved(x: np.ndarray, angle: np.ndarray, rotary_dim: int) -> np.ndarray:
+    """Rotate the pairs (2i, 2i+1), i < rotary_dim/2, of x [T, heads, D] by angle [T, rotary_dim/2];
+    the other dims pass through (float64)."""
+    x = np.asarray(x, np.float64)
+    c = np.cos(angle)[:, None, :]
+    s = np.sin(angle)[:, None, :]
+    out = x.copy()
+    a, b = x[..., 0:rotary_dim:2], x[..., 1:rotary_dim:2]
+    out[..., 0:rotary_dim:2] = a * c - b * s
+    out[..., 1:rotary_dim:2] = b * c + a * s
+    return out
+
+
 def qk_norm_rope(qkv: np.ndarray, num_q_heads: int, num_kv_heads: int, head_dim: int, rotary_dim: int,
                  q_norm_w: np.ndarray, k_norm_w: np.ndarray, eps: float, positions: np.ndarray,
-                 theta: float) -> np.ndarray:
+                 theta: float, neox: bool = True) -> np.ndarray:
     """qkv [T, (Hq + 2 Hkv) * D] (q heads, k heads, v heads) -> the same layout with the q
-    and k heads normalised and rotated; v unchanged. float64."""
+    and k heads normalised and rotated (rotate-half if neox, else interleaved); v
+    unchanged. float64."""
     qkv = np.asarray(qkv, np.float64)
     T = qkv.shape[0]
     D = head_dim
     heads = qkv.reshape(T, num_q_heads + 2 * num_kv_heads, D).copy()
     ang = rope_angles(positions, rotary_dim, theta)
+    rope = rope_half if neox else rope_interleaved
     q = heads[:, :num_q_heads]
     k = heads[:, num_q_heads:num_q_heads + num_kv_heads]
-    heads[:, :num_q_heads] = rope_half(head_rms_norm(q, q_norm_w, eps), ang, rotary_dim)
-    heads[:, num_q_heads:num_q_heads + num_kv_heads] = rope_half(head_rms_norm(k, k_norm_w, eps), ang, rotary_dim)
+    heads[:, :num_q_heads] = rope(head_rms_norm(q, q_norm_w, eps), ang, rotary_dim)
+    heads[:, num_q_heads:num_q_heads + num_kv_heads] = rope(head_rms_norm(k, k_norm_w, eps), ang, rotary_dim)
     return heads.reshape(T, -1)

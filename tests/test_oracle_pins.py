@@ -290,3 +290,22 @@ def test_qk_norm_rope_layout():
     assert np.allclose(heads[0, Hq], oracle.head_rms_norm(heads_in[0, Hq], kw, 1e-6))
     # dims past rotary_dim are the normalised values at every position
     assert np.allclose(heads[:, :Hq, rd:], oracle.head_rms_norm(heads_in[:, :Hq], qw, 1e-6)[..., rd:])
+
+
+def test_rope_interleaved_is_a_permuted_rope_half():
+    """Interleaved pairs (2i, 2i+1) become rotate-half pairs (i, i + rd/2) when the even
+    dims are moved to the front: the two arrangements differ only by that permutation."""
+    rng = np.random.default_rng(4)
+    D, rd = 16, 8
+    x = rng.standard_normal((3, 2, D))
+    ang = oracle.rope_angles(np.array([0, 7, 123]), rd, 500.0)
+    perm = np.concatenate([np.arange(0, rd, 2), np.arange(1, rd, 2), np.arange(rd, D)])
+    inv = np.argsort(perm)
+    via_half = oracle.rope_half(x[..., perm], ang, rd)[..., inv]
+    assert np.allclose(oracle.rope_interleaved(x, ang, rd), via_half, atol=1e-13)
+    # position 0 leaves x as it is; pair 0 at position p is (x0 + i x1) e^{i p}
+    assert np.array_equal(oracle.rope_interleaved(x[:1], ang[:1], rd), x[:1])
+    y = oracle.rope_interleaved(x, ang, rd)
+    z = (x[:, :, 0] + 1j * x[:, :, 1]) * np.exp(1j * np.array([0.0, 7.0, 123.0]))[:, None]
+    assert np.allclose(y[:, :, 0], z.real, atol=1e-12) and np.allclose(y[:, :, 1], z.imag, atol=1e-12)
+    assert np.array_equal(y[..., rd:], x[..., rd:])
