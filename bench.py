@@ -138,6 +138,42 @@ def router_timing(inp, x, steps):
             "bytes": nbytes, "timing": "graph replay"}
 
 
+def qk_norm_rope_timing(steps):
+    """The attention-side QK-Norm + RoPE step (moe_qk_norm_rope) on one GPU's share of GLM4-MoE
+    attention (12 q + 1 kv heads of 128, half of each rotated), fused and as two passes, at
+    the decode and prefill token counts; timed on graph replays of the call in place."""
+    import numpy as np
+    import torch
+    from shared_routed_expert_amd import _lib as L
+    from workloads import QK_CONFIGS, generate_qk
+    side = torch.cuda.Stream()
+    res = {}
+    for name in ("decode", "prefill"):
+        inp = generate_qk(QK_CONFIGS[name])
+        c = inp.cfg
+        qkv = torch.from_numpy(inp.qkv_bf16.view(np.int16)).cuda()
+        pos = torch.from_numpy(inp.positions).cuda()
+        qw, kw = torch.from_numpy(inp.q_norm_w).cuda(), torch.from_numpy(inp.k_norm_w).cuda()
+        cs = torch.empty((c.max_pos, c.rotary_dim), dtype=torch.float32, device="cuda")
+        L.moe_rope_cos_sin_table(cs, c.max_pos, c.rotary_dim, c.theta, side)
+        torch.cuda.synchronize()
+
+        def call(fused):
+            return lambda: L.moe_qk_norm_rope(qkv, c.T, c.num_q_heads, c.num_kv_heads, c.head_dim, c.rotary_dim,
+                                              c.neox, qw, kw, c.eps, pos, cs, c.max_pos, fused, side)
+        fused_us = graph_time([call(True)], side, steps)
+        unfused_us = graph_time([call(False)], side, steps)
+        # q and k heads read and written once, positions, the table rows, the two weight vectors
+        nbytes = 2 * c.T * (c.num_q_heads + c.num_kv_heads) * c.head_dim * 2 + c.T * 4 + c.T * c.rotary_dim * 4 \
+            + 2 * c.head_dim * 4
+        res[name] = {"T": c.T, "fused_us": round(fused_us, 2), "unfused_us": round(unfused_us, 2),
+                     "unfused_over_fused": round(unfused_us / fused_us, 3), "alg_bytes": nbytes,
+                     "fused_GBps": round(nbytes / fused_us / 1e3, 1),
+                     "fused_hbm_frac": round(nbytes / fused_us / 1e3 / HBM_PEAK_GBS, 4)}
+    res["timing"] = "graph replay"
+    return res
+
+
 GRAPH_ROUNDS = 8   # captured rounds per graph, so that the host's launch of a replay is amortised
 
 
@@ -359,6 +395,8 @@ def main():
     }
     log("bench: router gate (graph replays)")
     result["router_gate"] = router_timing(inp, x, args.steps)
+    log("bench: QK-Norm + RoPE, fused and unfused (graph replays)")
+    result["qk_norm_rope"] = qk_norm_rope_timing(args.steps)
     if not args.no_fusion_ab:
         log("bench: fused vs unfused layer (graph replays)")
         result["fusion_ab"] = fusion_ab(cfg, bm, x, logits, weights, layer, args.steps)

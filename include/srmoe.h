@@ -220,6 +220,38 @@ int moe_layer_forward(const uint16_t* x, const float* logits, const uint8_t* w13
                       size_t align_ws_bytes, void* ffn_ws, size_t ffn_ws_bytes, uint16_t* out,
                       void* stream);
 
+/* ---------------------------------------------------------------------------
+ * Attention side of the same model: the per-head QK norm fused with the rotary
+ * position embedding (intelliparadigm section 2.2; Optimizing GLM4-MoE for
+ * production section 2: both are per-head steps, so one kernel does both; GLM4-MoE
+ * rotates only part of each head).
+ *
+ * moe_qk_norm_rope works IN PLACE on qkv [T, (num_q_heads + 2*num_kv_heads) *
+ * head_dim] bf16, the qkv projection output (per token: the q heads, the k heads,
+ * the v heads). For every q and k head of token t (v heads are left untouched):
+ *     y = x / sqrt(mean(x^2) + eps) * w            (w = q_norm_w or k_norm_w, [head_dim] float32)
+ *     the first rotary_dim dims of y are rotated by angle(p, i) = p * theta^(-2i/rotary_dim),
+ *     i < rotary_dim/2, p = positions[t]; neox != 0 pairs dim i with i + rotary_dim/2
+ *     (rotate-half), neox == 0 pairs 2i with 2i+1 (interleaved); dims >= rotary_dim
+ *     keep y.
+ *   Float32 arithmetic, one bf16 rounding (round to nearest even) per value.
+ *   fused == 0 runs the two steps as two passes with y stored as bf16 in between (the
+ *   unfused form, for comparison).
+ *   positions [T] int32; a position outside [0, max_pos) is clamped into it.
+ *   cos_sin [max_pos, rotary_dim] float32: for each position rotary_dim/2 cosines
+ *   then rotary_dim/2 sines, as written by moe_rope_cos_sin_table.
+ *   limits: head_dim in {64, 128, 256}; rotary_dim a power of two, 16 <= rotary_dim
+ *   <= head_dim; num_q_heads + 2*num_kv_heads <= 1024; eps >= 0.
+ *   q_norm_w may be NULL when num_q_heads == 0, k_norm_w when num_kv_heads == 0.
+ * ------------------------------------------------------------------------- */
+int moe_qk_norm_rope(uint16_t* qkv, int T, int num_q_heads, int num_kv_heads, int head_dim, int rotary_dim,
+                     int neox, const float* q_norm_w, const float* k_norm_w, float eps,
+                     const int32_t* positions, const float* cos_sin, int max_pos, int fused, void* stream);
+/* cos_sin [max_pos, rotary_dim] float32 (device, written): cos_sin[p][i] = cos(a),
+ * cos_sin[p][rotary_dim/2 + i] = sin(a), a = p * theta^(-2i/rotary_dim), i < rotary_dim/2;
+ * computed in float64 and rounded to float32. rotary_dim even, theta > 1. */
+int moe_rope_cos_sin_table(float* cos_sin, int max_pos, int rotary_dim, double theta, void* stream);
+
 /* Host helpers. */
 size_t moe_sorted_capacity(int T, int K1, int E1, int block_m); /* P_max, rows */
 size_t moe_align_workspace_bytes(int T, int K1, int E1);

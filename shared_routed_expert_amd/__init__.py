@@ -10,7 +10,8 @@ _BINDING = ("lib", "LIB_PATH", "SrmoeError", "SCALE_PER_CHANNEL", "SCALE_BLOCK12
             "moe_route_topk_plus_shared", "moe_align_by_expert", "moe_fused_ffn", "moe_ffn_quant_x",
             "moe_ffn_gate_up", "moe_ffn_down", "moe_ffn_experts", "moe_ffn_experts_one_kernel",
             "moe_combine", "moe_layer_forward", "moe_sorted_capacity", "moe_align_workspace_bytes",
-            "moe_route_topk", "moe_combine_unfused", "moe_router_logits", "moe_router_workspace_bytes", "moe_ffn_workspace_bytes", "moe_ffn_workspace_offsets")
+            "moe_route_topk", "moe_combine_unfused", "moe_router_logits", "moe_router_workspace_bytes",
+            "moe_ffn_workspace_bytes", "moe_ffn_workspace_offsets", "moe_qk_norm_rope", "moe_rope_cos_sin_table")
 _LAYER = ("FusedMoE", "UnfusedMoE", "DeviceWeights")
 
 

@@ -46,6 +46,8 @@ def _load():
         "moe_router_workspace_bytes": ([I, I, I], Z),
         "moe_combine_unfused": ([I, I, I, P, Z, P, Z, P, P], I),
         "moe_layer_forward": ([P, P, P, P, P, P, I, I, I, I, I, I, F, I, P, P, P, P, P, P, P, P, Z, P, Z, P, P], I),
+        "moe_qk_norm_rope": ([P, I, I, I, I, I, I, P, P, F, P, P, I, I, P], I),
+        "moe_rope_cos_sin_table": ([P, I, I, ctypes.c_double, P], I),
         "moe_sorted_capacity": ([I, I, I, I], Z),
         "moe_align_workspace_bytes": ([I, I, I], Z),
         "moe_ffn_workspace_bytes": ([I, I, I, I, I, I, I], Z),
@@ -65,7 +67,7 @@ lib = _load()
 EXPORTED = ("moe_route_topk_plus_shared", "moe_align_by_expert", "moe_fused_ffn", "moe_ffn_quant_x",
             "moe_ffn_gate_up", "moe_ffn_down", "moe_ffn_experts", "moe_ffn_experts_one_kernel",
             "moe_combine", "moe_layer_forward", "moe_route_topk", "moe_combine_unfused", "moe_router_logits",
-            "moe_router_workspace_bytes", "moe_sorted_capacity",
+            "moe_router_workspace_bytes", "moe_qk_norm_rope", "moe_rope_cos_sin_table", "moe_sorted_capacity",
             "moe_align_workspace_bytes", "moe_ffn_workspace_bytes", "moe_ffn_workspace_offsets",
             "srmoe_status_string",
             "srmoe_last_hip_error")
@@ -209,3 +211,16 @@ def moe_layer_forward(x, logits, w13, s13, w2, s2, scale_mode, T, H, I, E, K, sh
                                _ptr(align_ws), align_ws_bytes, _ptr(ffn_ws), ffn_ws_bytes, _ptr(out),
                                _stream(stream))
     return _check("moe_layer_forward", st) if check else st
+
+
+def moe_qk_norm_rope(qkv, T, num_q_heads, num_kv_heads, head_dim, rotary_dim, neox, q_norm_w, k_norm_w, eps,
+                     positions, cos_sin, max_pos, fused=True, stream=None, check=True):
+    st = lib.moe_qk_norm_rope(_ptr(qkv), T, num_q_heads, num_kv_heads, head_dim, rotary_dim, int(neox),
+                              _ptr(q_norm_w), _ptr(k_norm_w), eps, _ptr(positions), _ptr(cos_sin), max_pos,
+                              int(fused), _stream(stream))
+    return _check("moe_qk_norm_rope", st) if check else st
+
+
+def moe_rope_cos_sin_table(cos_sin, max_pos, rotary_dim, theta, stream=None, check=True):
+    st = lib.moe_rope_cos_sin_table(_ptr(cos_sin), max_pos, rotary_dim, float(theta), _stream(stream))
+    return _check("moe_rope_cos_sin_table", st) if check else st

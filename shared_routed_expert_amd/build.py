@@ -12,7 +12,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libsrmoe.so")
-SOURCES = ["api.hip", "router.hip", "route.hip", "align.hip", "quant.hip", "ffn.hip", "ffn_decode.hip", "ffn_expert_decode.hip", "ffn_tile.hip", "front.hip"]
+SOURCES = ["api.hip", "router.hip", "route.hip", "align.hip", "quant.hip", "ffn.hip", "ffn_decode.hip", "ffn_expert_decode.hip", "ffn_tile.hip", "front.hip", "qknorm.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

@@ -41,6 +41,9 @@ hipError_t launch_expert_ffn_decode(const uint8_t*, const float*, const uint8_t*
                                     const uint8_t*, const float*, bool, int32_t*, int32_t*,
                                     const AlignOut*, const float*, float*, uint16_t*, int, int, int,
                                     int, int, hipStream_t);
+hipError_t launch_qk_norm_rope(uint16_t*, int, int, int, int, int, bool, const float*, const float*, float,
+                               const int32_t*, const float*, int, bool, hipStream_t);
+hipError_t launch_rope_table(float*, int, int, double, hipStream_t);
 }  // namespace srmoe
 
 using namespace srmoe;
@@ -413,6 +416,39 @@ int moe_combine_unfused(int T, int K, int H, const void* routed_ws, size_t route
   return hip_status(launch_combine(static_cast<const uint16_t*>(routed_ws),
                                    static_cast<const uint16_t*>(shared_ws), T, K, H, out,
                                    as_stream(stream)));
+}
+
+// head_dim in {64, 128, 256}; rotary_dim a power of two in [16, head_dim]
+static bool qk_dims_supported(int head_dim, int rotary_dim) {
+  if (head_dim != 64 && head_dim != 128 && head_dim != 256) return false;
+  return rotary_dim >= 16 && rotary_dim <= head_dim && (rotary_dim & (rotary_dim - 1)) == 0;
+}
+
+int moe_rope_cos_sin_table(float* cos_sin, int max_pos, int rotary_dim, double theta, void* stream) {
+  if (max_pos < 1 || rotary_dim < 2 || rotary_dim % 2 != 0 || !(theta > 1.0)) return SRMOE_ERR_INVALID_ARG;
+  if ((size_t)max_pos * rotary_dim >= ((size_t)1 << 31)) return SRMOE_ERR_UNSUPPORTED;
+  if (!cos_sin || !aligned16(cos_sin)) return SRMOE_ERR_INVALID_ARG;
+  return hip_status(launch_rope_table(cos_sin, max_pos, rotary_dim, theta, as_stream(stream)));
+}
+
+int moe_qk_norm_rope(uint16_t* qkv, int T, int num_q_heads, int num_kv_heads, int head_dim, int rotary_dim,
+                     int neox, const float* q_norm_w, const float* k_norm_w, float eps,
+                     const int32_t* positions, const float* cos_sin, int max_pos, int fused, void* stream) {
+  if (T < 0 || T > kMaxT || num_q_heads < 0 || num_kv_heads < 0 || num_q_heads + num_kv_heads < 1 ||
+      max_pos < 1 || !(eps >= 0.f) || !(eps < 1e30f))
+    return SRMOE_ERR_INVALID_ARG;
+  if (!qk_dims_supported(head_dim, rotary_dim) || num_q_heads + 2 * num_kv_heads > 1024)
+    return SRMOE_ERR_UNSUPPORTED;
+  if ((size_t)max_pos * rotary_dim >= ((size_t)1 << 31)) return SRMOE_ERR_UNSUPPORTED;
+  if (T == 0) return SRMOE_OK;
+  if (!qkv || !positions || !cos_sin || (num_q_heads > 0 && !q_norm_w) || (num_kv_heads > 0 && !k_norm_w))
+    return SRMOE_ERR_INVALID_ARG;
+  if (!aligned16(qkv) || !aligned16(positions) || !aligned16(cos_sin) || !aligned16(q_norm_w) ||
+      !aligned16(k_norm_w))
+    return SRMOE_ERR_INVALID_ARG;
+  return hip_status(launch_qk_norm_rope(qkv, T, num_q_heads, num_kv_heads, head_dim, rotary_dim, neox != 0,
+                                        q_norm_w, k_norm_w, eps, positions, cos_sin, max_pos, fused != 0,
+                                        as_stream(stream)));
 }
 
 }  // extern "C"

@@ -263,3 +263,26 @@ def test_layer_forward_rejects(L):
     assert f(align_ws_bytes=16) == -3
     assert f(ffn_ws_bytes=1024) == -3
     assert f(T=0, x=None, out=None) == 0
+
+
+def test_qk_norm_rope_rejects(L):
+    def f(**kw):
+        a = dict(qkv=FAKE, T=64, num_q_heads=12, num_kv_heads=1, head_dim=128, rotary_dim=64, neox=1,
+                 q_norm_w=FAKE, k_norm_w=FAKE, eps=1e-5, positions=FAKE, cos_sin=FAKE, max_pos=131072, fused=1)
+        a.update(kw)
+        return L.moe_qk_norm_rope(**a, stream=0, check=False)
+    assert f(T=-1) == -1 and f(num_q_heads=-1) == -1 and f(num_q_heads=0, num_kv_heads=0) == -1
+    assert f(max_pos=0) == -1 and f(eps=-1.0) == -1 and f(eps=float("nan")) == -1
+    assert f(head_dim=96) == -2 and f(rotary_dim=8) == -2 and f(rotary_dim=48) == -2
+    assert f(rotary_dim=256) == -2 and f(num_q_heads=1000, num_kv_heads=20) == -2
+    for name in ("qkv", "positions", "cos_sin", "q_norm_w", "k_norm_w"):
+        assert f(**{name: None}) == -1, name
+        assert f(**{name: MIS}) == -1, name
+    assert f(T=0, qkv=None, positions=None) == 0
+
+
+def test_rope_table_rejects(L):
+    f = lambda *a: L.moe_rope_cos_sin_table(*a, stream=0, check=False)
+    assert f(FAKE, 0, 64, 1e6) == -1 and f(FAKE, 16, 63, 1e6) == -1 and f(FAKE, 16, 64, 1.0) == -1
+    assert f(None, 16, 64, 1e6) == -1 and f(MIS, 16, 64, 1e6) == -1
+    assert f(FAKE, 1 << 26, 64, 1e6) == -2
