@@ -384,8 +384,8 @@ __global__ void __launch_bounds__(256, 2) down_tile_kernel(
 // stages its block's 128 a_q rows (zero-filled from I to the K-step boundary)
 // and the w2 scales of its columns in LDS once; each wavefront then sweeps
 // kDownTiles 64-column tiles of w2[e] for one 64-row half, with the weights as
-// the MFMA A operand, loading each weight K slice for the next tile as soon as
-// the MFMAs of the current tile have consumed it. Inside a tile, row r of MFMA
+// the MFMA A operand and two tiles' weight fragments in registers (a tile's set is
+// refilled two tiles ahead as soon as its MFMAs have consumed it). Inside a tile, row r of MFMA
 // tile n holds column (r / 4) * 16 + 4 * n + r % 4, so each lane ends with 16
 // consecutive output columns of a row. The bf16 tile then goes through a
 // wavefront-private LDS buffer so that 8 lanes write each row's 128 contiguous
@@ -481,25 +481,30 @@ __global__ void __launch_bounds__(256, 2) down_wide_kernel(
   const int t0 = active ? t : 0;
   // weight fragment rows: row r16 of MFMA tile n is column (r16/4)*16 + 4n + r16%4
   const uint8_t* wb = w2 + (size_t)e * H * I + (size_t)((r16 >> 2) * 16 + (r16 & 3)) * I;
-  v8i wf[4][KS];
+  // two register sets of weight fragments: tile j computes from set j & 1 while the set
+  // of tile j + 1 is in flight, and set j & 1 is refilled with tile j + 2 as soon as its
+  // MFMAs have consumed it
+  v8i wf[2][4][KS];
+  auto wload = [&](v8i (&w)[4][KS], int tile) __attribute__((always_inline)) {
 #pragma unroll
-  for (int n = 0; n < 4; ++n)
+    for (int n = 0; n < 4; ++n)
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) wf[n][ks] = load32(wb + (size_t)(t0 * 64 + 4 * n) * I + koff[ks]);
+      for (int ks = 0; ks < KS; ++ks) w[n][ks] = load32(wb + (size_t)(tile * 64 + 4 * n) * I + koff[ks]);
+  };
+  wload(wf[0], t0);
+  wload(wf[1], min(t0 + 2, nct - 1));
   __syncthreads();   // the a_q tile and the scales are in LDS
   if (!active) return;
-  // Drain the prologue's loads (the first MFMAs need them anyway) so that the
-  // loop entry carries no pending loads; otherwise the waits inside the loop are
-  // placed for the worse of both paths and also cover the previous tile's stores.
-  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0), expcnt and lgkmcnt unconstrained
 
   const v4f zero4 = {0.f, 0.f, 0.f, 0.f};
   const uint8_t* trow = &atile[(64 * wt + r16) * kDownLD + kq * 32];
   uint8_t* stg = stage[wv];
+#pragma unroll
   for (int j = 0; j < kDownTiles; ++j) {
-    const int tn = t + 2;
-    const bool more = j + 1 < kDownTiles && tn < nct;
-    const int tl = more ? tn : t;   // tile whose weights are fetched next (re-read at the end)
+    const int cur = j & 1;
+    const int tj = t + 2 * j;
+    if (tj >= nct) break;
+    const int tl = min(tj + 4, nct - 1);   // the tile two steps ahead (re-read past the end)
     v4f acc[4][4];   // [column tile n][row tile m]
 #pragma unroll
     for (int n = 0; n < 4; ++n)
@@ -510,33 +515,31 @@ __global__ void __launch_bounds__(256, 2) down_wide_kernel(
       v8i tf[4];
 #pragma unroll
       for (int m = 0; m < 4; ++m) tf[m] = load32(trow + 16 * m * kDownLD + ks * kGroup);
-      const float sb = kBlock ? scol[((t * 64 - c0) / kGroup) * KS + ks] : 1.f;
+      const float sb = kBlock ? scol[((tj * 64 - c0) / kGroup) * KS + ks] : 1.f;
 #pragma unroll
       for (int m = 0; m < 4; ++m)
 #pragma unroll
         for (int n = 0; n < 4; ++n) {
           if (!kBlock) {
-            acc[n][m] = mfma_16x16x128_fp8(wf[n][ks], tf[m], acc[n][m]);
+            acc[n][m] = mfma_16x16x128_fp8(wf[cur][n][ks], tf[m], acc[n][m]);
           } else {
-            const v4f p4 = mfma_16x16x128_fp8(wf[n][ks], tf[m], zero4);
+            const v4f p4 = mfma_16x16x128_fp8(wf[cur][n][ks], tf[m], zero4);
             const float sc = sar[m][ks] * sb;
 #pragma unroll
             for (int q = 0; q < 4; ++q) acc[n][m][q] += p4[q] * sc;
           }
         }
       __builtin_amdgcn_sched_barrier(0);
-      // the next tile's slice ks replaces the one just consumed
-#pragma unroll
-      for (int n = 0; n < 4; ++n) wf[n][ks] = load32(wb + (size_t)(tl * 64 + 4 * n) * I + koff[ks]);
-      __builtin_amdgcn_sched_barrier(0);
     }
+    if (j + 2 < kDownTiles) wload(wf[cur], tl);
+    __builtin_amdgcn_sched_barrier(0);
     // scale, round and stage: lane (r16, kq) holds columns 16 kq .. 16 kq + 15 of
     // rows 16 m + r16 of the wavefront's 64
     float swc[16];
 #pragma unroll
     for (int c = 0; c < 16; c += 4) {
       const float4 v = kBlock ? make_float4(1.f, 1.f, 1.f, 1.f)
-                              : *reinterpret_cast<const float4*>(&scol[t * 64 - c0 + 16 * kq + c]);
+                              : *reinterpret_cast<const float4*>(&scol[tj * 64 - c0 + 16 * kq + c]);
       swc[c] = v.x; swc[c + 1] = v.y; swc[c + 2] = v.z; swc[c + 3] = v.w;
     }
 #pragma unroll
@@ -554,15 +557,13 @@ __global__ void __launch_bounds__(256, 2) down_wide_kernel(
     }
     // store: 8 lanes per row, 8 rows per instruction, each row's 128 bytes whole
     // (a wavefront's LDS operations complete in order, so no barrier is needed)
-    const int hs = t * 64 + (lane & 7) * 8;
+    const int hs = tj * 64 + (lane & 7) * 8;
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
       const uint4 v = *reinterpret_cast<const uint4*>(stg + (8 * q + (lane >> 3)) * kStageLD + (lane & 7) * 16);
       const u32x4_nt nv = {v.x, v.y, v.z, v.w};
       __builtin_nontemporal_store(nv, reinterpret_cast<u32x4_nt*>(slot_out + (size_t)srow[q] * H + hs));
     }
-    if (!more) break;
-    t = tn;
   }
 }
 
