@@ -44,11 +44,15 @@ __device__ __forceinline__ uint32_t e4m3_encode(float v) {
   return code | sign;
 }
 
-// float -> bfloat16 bits, round to nearest even (finite inputs).
-__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
+// float -> bfloat16 bits, round to nearest even (finite inputs): gfx950 converts in
+// hardware (v_cvt_pk_bf16_f32, two values per instruction, in the current rounding
+// mode, which is to nearest even).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
+// two floats -> their bf16 bits packed in one word (lo in bits 0..15)
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  const bf16x2_t v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
 }
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t b) { return __uint_as_float(b << 16); }

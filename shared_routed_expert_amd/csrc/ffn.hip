@@ -233,7 +233,7 @@ __global__ void __launch_bounds__(256) down_kernel(
       // column c = 4 * n + j of this lane's 16
       const float y0 = acc[c >> 2][m][c & 3] * sw[c] * r;
       const float y1 = acc[(c + 1) >> 2][m][(c + 1) & 3] * sw[c + 1] * r;
-      packed[c >> 1] = (uint32_t)f32_to_bf16(y0) | ((uint32_t)f32_to_bf16(y1) << 16);
+      packed[c >> 1] = pack_bf16x2(y0, y1);
     }
     uint4* dst = reinterpret_cast<uint4*>(slot_out + (size_t)s * H + h0 + kq * 16);
     dst[0] = make_uint4(packed[0], packed[1], packed[2], packed[3]);
@@ -340,10 +340,10 @@ __global__ void __launch_bounds__(256) combine_kernel(const uint16_t* __restrict
     }
   }
   uint4 o;
-  o.x = f32_to_bf16(acc[0]) | ((uint32_t)f32_to_bf16(acc[1]) << 16);
-  o.y = f32_to_bf16(acc[2]) | ((uint32_t)f32_to_bf16(acc[3]) << 16);
-  o.z = f32_to_bf16(acc[4]) | ((uint32_t)f32_to_bf16(acc[5]) << 16);
-  o.w = f32_to_bf16(acc[6]) | ((uint32_t)f32_to_bf16(acc[7]) << 16);
+  o.x = pack_bf16x2(acc[0], acc[1]);
+  o.y = pack_bf16x2(acc[2], acc[3]);
+  o.z = pack_bf16x2(acc[4], acc[5]);
+  o.w = pack_bf16x2(acc[6], acc[7]);
   *reinterpret_cast<uint4*>(out + t * H + h) = o;
 }
 

@@ -252,7 +252,7 @@ __global__ void __launch_bounds__(256) down_decode_kernel(
   for (int c = 0; c < 16; c += 2) {   // column c = 4 * n + j of this lane's 16
     const float y0 = acc[c >> 2][c & 3] * sw[c] * rsc;
     const float y1 = acc[(c + 1) >> 2][(c + 1) & 3] * sw[c + 1] * rsc;
-    packed[c >> 1] = (uint32_t)f32_to_bf16(y0) | ((uint32_t)f32_to_bf16(y1) << 16);
+    packed[c >> 1] = pack_bf16x2(y0, y1);
   }
   uint4* dst = reinterpret_cast<uint4*>(slot_out + (size_t)srow * H + h0 + kq * 16);
   dst[0] = make_uint4(packed[0], packed[1], packed[2], packed[3]);

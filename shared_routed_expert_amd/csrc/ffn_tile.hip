@@ -372,7 +372,7 @@ __global__ void __launch_bounds__(256, 2) down_tile_kernel(
     for (int c = 0; c < 16; c += 2) {   // column c = 4 * n + j of this lane's 16
       const float y0 = acc[c >> 2][m][c & 3] * swc[c] * rsc[m];
       const float y1 = acc[(c + 1) >> 2][m][(c + 1) & 3] * swc[c + 1] * rsc[m];
-      packed[c >> 1] = (uint32_t)f32_to_bf16(y0) | ((uint32_t)f32_to_bf16(y1) << 16);
+      packed[c >> 1] = pack_bf16x2(y0, y1);
     }
     uint4* dst = reinterpret_cast<uint4*>(slot_out + (size_t)s * H + hl);
     dst[0] = make_uint4(packed[0], packed[1], packed[2], packed[3]);
@@ -549,7 +549,7 @@ __global__ void __launch_bounds__(256, 2) down_wide_kernel(
       for (int c = 0; c < 16; c += 2) {   // column c = 4 * n + q of this lane's 16
         const float y0 = acc[c >> 2][m][c & 3] * swc[c] * rsc[m];
         const float y1 = acc[(c + 1) >> 2][m][(c + 1) & 3] * swc[c + 1] * rsc[m];
-        packed[c >> 1] = (uint32_t)f32_to_bf16(y0) | ((uint32_t)f32_to_bf16(y1) << 16);
+        packed[c >> 1] = pack_bf16x2(y0, y1);
       }
       uint4* sp = reinterpret_cast<uint4*>(stg + (16 * m + r16) * kStageLD + kq * 32);
       sp[0] = make_uint4(packed[0], packed[1], packed[2], packed[3]);
