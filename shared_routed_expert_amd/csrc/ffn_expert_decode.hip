@@ -384,8 +384,10 @@ __global__ void __launch_bounds__(512) expert_ffn_decode_kernel(
     const float wgt = wgt_s[r];
     // per channel: the row's 32 threads; block: the 128 / C threads of a 128-column group
     const float scale = fp8_scale(group_max(amax, kBlock ? kGroup / C : 32));
+    const ScaleDiv q = scale_div(scale);
 #pragma unroll
-    for (int m = 0; m < C; ++m) aqs[r * AS + part * C + m] = (uint8_t)e4m3_encode(__fdiv_rn(av[m], scale));
+    for (int m = 0; m < C; m += 2)   // C = I / 32 is even
+      *reinterpret_cast<uint16_t*>(&aqs[r * AS + part * C + m]) = (uint16_t)quant2(q, av[m], av[m + 1]);
     if (!kBlock) {
       if (part == 0) rsc_s[r] = wgt * scale;
     } else {

@@ -85,9 +85,8 @@ __device__ __forceinline__ void route_token_wave(const float* __restrict__ logit
 }
 
 // ----------------------------------------------------------------------------- x quantisation
-__device__ __forceinline__ uint32_t encode4(float a, float b, float c, float d, float s) {
-  return e4m3_encode(__fdiv_rn(a, s)) | (e4m3_encode(__fdiv_rn(b, s)) << 8) |
-         (e4m3_encode(__fdiv_rn(c, s)) << 16) | (e4m3_encode(__fdiv_rn(d, s)) << 24);
+__device__ __forceinline__ uint32_t encode4(float a, float b, float c, float d, const ScaleDiv& q) {
+  return quant2(q, a, b) | (quant2(q, c, d) << 16);
 }
 
 __device__ __forceinline__ float4 load_bf16x4(const uint16_t* p) {
@@ -130,14 +129,15 @@ __device__ __forceinline__ void quant_x_token(const uint16_t* __restrict__ x, in
     const float scale = fp8_scale(fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3])));
     if (!valid) return;
     if (tid == 0) sx[t] = scale;
+    const ScaleDiv q = scale_div(scale);
 #pragma unroll
     for (int i = 0; i < kMaxStripes; ++i) {
       const int h = i * 1024 + tid * 4;
-      if (h < H) *reinterpret_cast<uint32_t*>(qrow + h) = encode4(v[i].x, v[i].y, v[i].z, v[i].w, scale);
+      if (h < H) *reinterpret_cast<uint32_t*>(qrow + h) = encode4(v[i].x, v[i].y, v[i].z, v[i].w, q);
     }
     for (int h = kMaxStripes * 1024 + tid * 4; h < H; h += 1024) {
       const float4 u = load_bf16x4(row + h);
-      *reinterpret_cast<uint32_t*>(qrow + h) = encode4(u.x, u.y, u.z, u.w, scale);
+      *reinterpret_cast<uint32_t*>(qrow + h) = encode4(u.x, u.y, u.z, u.w, q);
     }
   } else {
     if (!valid) return;
@@ -148,7 +148,7 @@ __device__ __forceinline__ void quant_x_token(const uint16_t* __restrict__ x, in
       const float4 v = in ? load_bf16x4(row + h) : make_float4(0.f, 0.f, 0.f, 0.f);
       const float scale = fp8_scale(group_max(amax4(v), 32));
       if (in && (tid & 31) == 0) sx[(size_t)t * (H / kGroup) + h / kGroup] = scale;
-      if (in) *reinterpret_cast<uint32_t*>(qrow + h) = encode4(v.x, v.y, v.z, v.w, scale);
+      if (in) *reinterpret_cast<uint32_t*>(qrow + h) = encode4(v.x, v.y, v.z, v.w, scale_div(scale));
     }
   }
 }

@@ -60,17 +60,16 @@ __global__ void __launch_bounds__(256) quant_a_kernel(const float* __restrict__ 
       sa[p] = scale;
       row_scale[p] = wgt * scale;
     }
+    const ScaleDiv q = scale_div(scale);
 #pragma unroll
     for (int j = 0; j < kMaxStripes; ++j) {
       const int i = j * 32 + part * 2;
       if (i < I)
-        *reinterpret_cast<uint16_t*>(qrow + i) =
-            (uint16_t)(e4m3_encode(__fdiv_rn(v[j].x, scale)) | (e4m3_encode(__fdiv_rn(v[j].y, scale)) << 8));
+        *reinterpret_cast<uint16_t*>(qrow + i) = (uint16_t)quant2(q, v[j].x, v[j].y);
     }
     for (int i = kMaxStripes * 32 + part * 2; i < I; i += 32) {
       const float2 w = *reinterpret_cast<const float2*>(row + i);
-      *reinterpret_cast<uint16_t*>(qrow + i) =
-          (uint16_t)(e4m3_encode(__fdiv_rn(w.x, scale)) | (e4m3_encode(__fdiv_rn(w.y, scale)) << 8));
+      *reinterpret_cast<uint16_t*>(qrow + i) = (uint16_t)quant2(q, w.x, w.y);
     }
   } else {
     if (part == 0) row_scale[p] = wgt;
@@ -84,10 +83,10 @@ __global__ void __launch_bounds__(256) quant_a_kernel(const float* __restrict__ 
       }
       const float scale = fp8_scale(row16_max(amax));
       if (part == 0) sa[(size_t)p * (I / kGroup) + g / kGroup] = scale;
+      const ScaleDiv q = scale_div(scale);
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        *reinterpret_cast<uint16_t*>(qrow + g + part * 2 + 32 * j) =
-            (uint16_t)(e4m3_encode(__fdiv_rn(v[j].x, scale)) | (e4m3_encode(__fdiv_rn(v[j].y, scale)) << 8));
+        *reinterpret_cast<uint16_t*>(qrow + g + part * 2 + 32 * j) = (uint16_t)quant2(q, v[j].x, v[j].y);
     }
   }
 }
