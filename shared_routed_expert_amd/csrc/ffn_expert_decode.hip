@@ -19,7 +19,8 @@
 //           a group's 64 rows of w2[e] are 64 * I contiguous bytes, loaded as
 //           1 KB runs and passed through LDS into the swap-AB fragment layout
 //           (weights as the A operand, a_q as B), the next group loading while
-//           one is multiplied. Weighted bf16 rows go to slot_out.
+//           one is multiplied. The weighted bf16 rows pass through LDS once more so
+//           that every store writes whole 128-byte row pieces to slot_out.
 //
 // The split kernels stream the same weights but pass a through HBM, quantise it in
 // a pass of their own and re-read it; here the down GEMM takes a_q from LDS and
@@ -43,6 +44,7 @@ constexpr int kXMaxH = 5120;                    // largest H whose x rows fit th
 constexpr int kXMaxHB = kXMaxH / kGroup;
 constexpr int kRunK = 1024;                     // K bytes of a phase-1 batch per row
 constexpr int kHalfRS = kRunK / 2 + 16;         // LDS row stride of a staged half batch
+constexpr int kOutRS = 128 + 16;                // LDS row stride of a staged group of output rows
 
 // Raw buffer resource over [base, base + bytes) (GFX9 descriptor word 3); loads at
 // offsets past `bytes` return zero.
@@ -64,8 +66,10 @@ struct ExpertDecodeLds {
   static constexpr int kStage1 = 8 * 16 * kHalfRS;              // per-wavefront half batches (phase 1)
   static constexpr int kGU = 16 * (2 * I + 4) * 4;              // g|u float32 (phase 1 -> 2)
   static constexpr int kStage3 = 8 * 64 * (I + 16);             // per-wavefront w2 groups (phase 3)
-  static constexpr int kBig = (kX + kStage1) > kStage3 ? ((kX + kStage1) > kGU ? kX + kStage1 : kGU)
-                                                       : (kStage3 > kGU ? kStage3 : kGU);
+  static constexpr int kOut = 8 * 8 * kOutRS;                    // per-wavefront output rows (phase 3)
+  static constexpr int kP3 = kStage3 + kOut;
+  static constexpr int kBig = (kX + kStage1) > kP3 ? ((kX + kStage1) > kGU ? kX + kStage1 : kGU)
+                                                   : (kP3 > kGU ? kP3 : kGU);
 };
 
 // The in-kernel align (kAlign): every workgroup derives the expert-sorted layout of
@@ -406,6 +410,7 @@ __global__ void __launch_bounds__(512) expert_ffn_decode_kernel(
 
   // ---- phase 3: down
   uint8_t* stg3 = big + wv * 64 * AS;
+  uint8_t* ost = big + Lds::kStage3 + wv * 8 * kOutRS;
   uint32_t kc[2];
   v8i avq[2];
   float sr[2] = {0.f, 0.f};
@@ -420,7 +425,6 @@ __global__ void __launch_bounds__(512) expert_ffn_decode_kernel(
     if (kBlock && u * kGroup < I) sr[u] = sa_s[r16][u];
   }
   const float rsc = rsc_s[r16];
-  const int srow = srow_s[r16];
   // lane's LDS slot for each 16-byte piece of a group: column c = o / I of the 64 goes to
   // row 16 ((c / 4) % 4) + 4 (c / 16) + c % 4 so that MFMA tile n reads rows 16 n .. 16 n + 15
   int soff[NI];
@@ -459,7 +463,7 @@ __global__ void __launch_bounds__(512) expert_ffn_decode_kernel(
 #pragma unroll
     for (int n = 0; n < 4; ++n) asm volatile("" : "+v"(d[n]));
     const int h0 = group_of(i) * 64;
-    if (h0 >= H || srow >= sentinel) return;
+    if (h0 >= H) return;   // uniform: past the wavefront's groups
     float sw[16];
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
@@ -475,9 +479,20 @@ __global__ void __launch_bounds__(512) expert_ffn_decode_kernel(
       const float y1 = d[(c + 1) >> 2][(c + 1) & 3] * sw[c + 1] * rsc;
       packed[c >> 1] = pack_bf16x2(y0, y1);
     }
-    uint4* dst = reinterpret_cast<uint4*>(slot_out + (size_t)srow * H + h0 + kq * 16);
-    dst[0] = make_uint4(packed[0], packed[1], packed[2], packed[3]);
-    dst[1] = make_uint4(packed[4], packed[5], packed[6], packed[7]);
+    // through the wavefront's 8 LDS rows, 8 output rows at a time, so that each store
+    // writes 8 rows x 128 whole bytes (a wavefront's LDS operations complete in order);
+    // padding rows are not stored
+#pragma unroll
+    for (int ps = 0; ps < 2; ++ps) {
+      if ((r16 >> 3) == ps) {
+        uint4* sp = reinterpret_cast<uint4*>(ost + (r16 & 7) * kOutRS + kq * 32);
+        sp[0] = make_uint4(packed[0], packed[1], packed[2], packed[3]);
+        sp[1] = make_uint4(packed[4], packed[5], packed[6], packed[7]);
+      }
+      const int sr = srow_s[8 * ps + (lane >> 3)];
+      const uint4 v = *reinterpret_cast<const uint4*>(ost + (lane >> 3) * kOutRS + (lane & 7) * 16);
+      if (sr < sentinel) *reinterpret_cast<uint4*>(slot_out + (size_t)sr * H + h0 + (lane & 7) * 8) = v;
+    }
   };
 #pragma unroll 1
   for (int i = 0; i < n_my; i += 2) {
