@@ -138,6 +138,38 @@ def router_timing(inp, x, steps):
             "bytes": nbytes, "timing": "graph replay"}
 
 
+def from_x_timing(inp, x, layer, weights, steps):
+    """Routing and the whole layer from x (the router gate folded into the route call):
+    moe_route_from_x, and moe_layer_forward_from_x against moe_router_logits +
+    moe_layer_forward; timed on graph replays over the cycled weight sets."""
+    import torch
+    from shared_routed_expert_amd import _lib as L
+    c = inp.cfg
+    w = torch.from_numpy(inp.router_w).cuda()
+    bias = torch.from_numpy(inp.bias).cuda() if inp.bias.any() else None
+    side = torch.cuda.Stream()
+    rwb = L.moe_route_from_x_workspace_bytes(c.T, c.H, c.E)
+    rws = torch.empty(rwb, dtype=torch.uint8, device="cuda")
+    ids = torch.empty((c.T, c.K1), dtype=torch.int32, device="cuda")
+    tw = torch.empty((c.T, c.K1), dtype=torch.float32, device="cuda")
+    route_us = graph_time([lambda: L.moe_route_from_x(x, w, bias, c.T, c.H, c.E, c.K, 1.0, ids, tw, rws, rwb,
+                                                      side)], side, steps)
+    lg = torch.empty((c.T, c.E), dtype=torch.float32, device="cuda")
+    wsb = L.moe_router_workspace_bytes(c.T, c.H, c.E)
+    ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device="cuda")
+
+    def two_calls(Wt):
+        def f():
+            L.moe_router_logits(x, w, bias, c.T, c.H, c.E, lg, ws, wsb, side)
+            layer.forward_fused(x, lg, Wt, 1.0, side)
+        return f
+    sep_us = graph_time([two_calls(Wt) for Wt in weights], side, steps)
+    fold_us = graph_time([(lambda Wt=Wt: layer.forward_from_x(x, w, bias, Wt, 1.0, side)) for Wt in weights], side,
+                         steps)
+    return {"route_from_x_us": round(route_us, 2), "layer_from_x_us": round(fold_us, 2),
+            "gate_then_layer_us": round(sep_us, 2), "timing": "graph replay"}
+
+
 def qk_norm_rope_timing(steps):
     """The attention-side QK-Norm + RoPE step (moe_qk_norm_rope) on one GPU's share of GLM4-MoE
     attention (12 q + 1 kv heads of 128, half of each rotated), fused and as two passes, at
@@ -395,6 +427,8 @@ def main():
     }
     log("bench: router gate (graph replays)")
     result["router_gate"] = router_timing(inp, x, args.steps)
+    log("bench: routing and the layer from x (graph replays)")
+    result["from_x"] = from_x_timing(inp, x, layer, weights, args.steps)
     log("bench: QK-Norm + RoPE, fused and unfused (graph replays)")
     result["qk_norm_rope"] = qk_norm_rope_timing(args.steps)
     if not args.no_fusion_ab:

@@ -93,6 +93,35 @@ int moe_router_logits(const uint16_t* x, const float* w_router, const float* bia
 size_t moe_router_workspace_bytes(int T, int H, int E); /* host */
 
 /* ---------------------------------------------------------------------------
+ * The router gate folded into the route call: routing straight from x.
+ * moe_route_from_x = the gate of moe_router_logits followed by the routing of
+ * moe_route_topk_plus_shared, with the gate's K-split partial tiles summed inside the
+ * routing kernel (in chunk order, then + bias: the same float32 operations as the gate's
+ * own reduction), so ids and weights equal those of the two calls bit for bit, one
+ * launch and one [T,E] round trip fewer. Arguments as in those two calls;
+ * workspace >= moe_route_from_x_workspace_bytes(T,H,E) bytes (device): the partial
+ * tiles, or the logits when the gate runs in one K chunk.
+ * limits: H % 128 == 0, 1 <= E <= 255, 0 <= K <= min(E, 15).
+ * ------------------------------------------------------------------------- */
+int moe_route_from_x(const uint16_t* x, const float* w_router, const float* bias, int T, int H, int E, int K,
+                     float shared_weight, int32_t* topk_ids, float* topk_w, void* workspace, size_t ws_bytes,
+                     void* stream);
+size_t moe_route_from_x_workspace_bytes(int T, int H, int E); /* host; 0 for empty shapes */
+
+/* The whole layer from x: moe_layer_forward with the router gate in front of it and the
+ * gate's partial tiles summed by the routing part of its first launch (so the outputs
+ * equal moe_router_logits + moe_layer_forward bit for bit). router_ws as for
+ * moe_route_from_x; every other argument as for moe_layer_forward. */
+int moe_layer_forward_from_x(const uint16_t* x, const float* w_router, const float* bias,
+                             const uint8_t* w13, const float* s13, const uint8_t* w2, const float* s2,
+                             int scale_mode, int T, int H, int I, int E, int K, float shared_weight,
+                             int block_m, int32_t* topk_ids, float* topk_w, int32_t* sorted_slot_ids,
+                             int32_t* block_expert, int32_t* expert_counts, int32_t* expert_offsets,
+                             int32_t* num_padded, void* router_ws, size_t router_ws_bytes, void* align_ws,
+                             size_t align_ws_bytes, void* ffn_ws, size_t ffn_ws_bytes, uint16_t* out,
+                             void* stream);
+
+/* ---------------------------------------------------------------------------
  * The unfused layer, for the fused-vs-unfused comparison: the routed experts and
  * the shared expert computed as two passes and added (the pages' formulation
  * before the fusion: intelliparadigm section 2.1, shared output plus the weighted

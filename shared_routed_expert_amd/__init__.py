@@ -11,7 +11,8 @@ _BINDING = ("lib", "LIB_PATH", "SrmoeError", "SCALE_PER_CHANNEL", "SCALE_BLOCK12
             "moe_ffn_gate_up", "moe_ffn_down", "moe_ffn_experts", "moe_ffn_experts_one_kernel",
             "moe_combine", "moe_layer_forward", "moe_sorted_capacity", "moe_align_workspace_bytes",
             "moe_route_topk", "moe_combine_unfused", "moe_router_logits", "moe_router_workspace_bytes",
-            "moe_ffn_workspace_bytes", "moe_ffn_workspace_offsets", "moe_qk_norm_rope", "moe_rope_cos_sin_table")
+            "moe_ffn_workspace_bytes", "moe_ffn_workspace_offsets", "moe_qk_norm_rope", "moe_rope_cos_sin_table",
+            "moe_route_from_x", "moe_route_from_x_workspace_bytes", "moe_layer_forward_from_x")
 _LAYER = ("FusedMoE", "UnfusedMoE", "DeviceWeights")
 
 

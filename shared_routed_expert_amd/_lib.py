@@ -47,6 +47,10 @@ def _load():
         "moe_combine_unfused": ([I, I, I, P, Z, P, Z, P, P], I),
         "moe_layer_forward": ([P, P, P, P, P, P, I, I, I, I, I, I, F, I, P, P, P, P, P, P, P, P, Z, P, Z, P, P], I),
         "moe_qk_norm_rope": ([P, I, I, I, I, I, I, P, P, F, P, P, I, I, P], I),
+        "moe_route_from_x": ([P, P, P, I, I, I, I, F, P, P, P, Z, P], I),
+        "moe_route_from_x_workspace_bytes": ([I, I, I], Z),
+        "moe_layer_forward_from_x": ([P, P, P, P, P, P, P, I, I, I, I, I, I, F, I, P, P, P, P, P, P, P, P, Z, P, Z,
+                                      P, Z, P, P], I),
         "moe_rope_cos_sin_table": ([P, I, I, ctypes.c_double, P], I),
         "moe_sorted_capacity": ([I, I, I, I], Z),
         "moe_align_workspace_bytes": ([I, I, I], Z),
@@ -67,7 +71,8 @@ lib = _load()
 EXPORTED = ("moe_route_topk_plus_shared", "moe_align_by_expert", "moe_fused_ffn", "moe_ffn_quant_x",
             "moe_ffn_gate_up", "moe_ffn_down", "moe_ffn_experts", "moe_ffn_experts_one_kernel",
             "moe_combine", "moe_layer_forward", "moe_route_topk", "moe_combine_unfused", "moe_router_logits",
-            "moe_router_workspace_bytes", "moe_qk_norm_rope", "moe_rope_cos_sin_table", "moe_sorted_capacity",
+            "moe_router_workspace_bytes", "moe_qk_norm_rope", "moe_rope_cos_sin_table", "moe_route_from_x",
+            "moe_route_from_x_workspace_bytes", "moe_layer_forward_from_x", "moe_sorted_capacity",
             "moe_align_workspace_bytes", "moe_ffn_workspace_bytes", "moe_ffn_workspace_offsets",
             "srmoe_status_string",
             "srmoe_last_hip_error")
@@ -224,3 +229,26 @@ def moe_qk_norm_rope(qkv, T, num_q_heads, num_kv_heads, head_dim, rotary_dim, ne
 def moe_rope_cos_sin_table(cos_sin, max_pos, rotary_dim, theta, stream=None, check=True):
     st = lib.moe_rope_cos_sin_table(_ptr(cos_sin), max_pos, rotary_dim, float(theta), _stream(stream))
     return _check("moe_rope_cos_sin_table", st) if check else st
+
+
+def moe_route_from_x_workspace_bytes(T, H, E):
+    return lib.moe_route_from_x_workspace_bytes(T, H, E)
+
+
+def moe_route_from_x(x, w_router, bias, T, H, E, K, shared_weight, topk_ids, topk_w, workspace, ws_bytes,
+                     stream=None, check=True):
+    st = lib.moe_route_from_x(_ptr(x), _ptr(w_router), _ptr(bias), T, H, E, K, shared_weight, _ptr(topk_ids),
+                              _ptr(topk_w), _ptr(workspace), ws_bytes, _stream(stream))
+    return _check("moe_route_from_x", st) if check else st
+
+
+def moe_layer_forward_from_x(x, w_router, bias, w13, s13, w2, s2, scale_mode, T, H, I, E, K, shared_weight,
+                             block_m, topk_ids, topk_w, sorted_slot_ids, block_expert, expert_counts,
+                             expert_offsets, num_padded, router_ws, router_ws_bytes, align_ws, align_ws_bytes,
+                             ffn_ws, ffn_ws_bytes, out, stream=None, check=True):
+    st = lib.moe_layer_forward_from_x(
+        _ptr(x), _ptr(w_router), _ptr(bias), _ptr(w13), _ptr(s13), _ptr(w2), _ptr(s2), scale_mode, T, H, I, E, K,
+        shared_weight, block_m, _ptr(topk_ids), _ptr(topk_w), _ptr(sorted_slot_ids), _ptr(block_expert),
+        _ptr(expert_counts), _ptr(expert_offsets), _ptr(num_padded), _ptr(router_ws), router_ws_bytes,
+        _ptr(align_ws), align_ws_bytes, _ptr(ffn_ws), ffn_ws_bytes, _ptr(out), _stream(stream))
+    return _check("moe_layer_forward_from_x", st) if check else st

@@ -2,12 +2,16 @@
 // layout and kernel launches on the caller's stream. See include/srmoe.h.
 #include "srmoe.h"
 
-#include "common.hpp"
+#include <functional>
+
+#include "front_dev.hpp"
 
 namespace srmoe {
-hipError_t launch_route(const float*, int, int, int, float, int32_t*, float*, hipStream_t);
+hipError_t launch_route(const LogitSrc&, int, int, int, float, int32_t*, float*, hipStream_t);
 hipError_t launch_route_topk(const float*, int, int, int, int32_t*, float*, hipStream_t);
 size_t router_workspace_bytes(int T, int H, int E);
+int router_splits(int T, int H, int E);
+hipError_t launch_router_gemm(const uint16_t*, const float*, const float*, int, int, int, float*, hipStream_t);
 hipError_t launch_router(const uint16_t*, const float*, const float*, int, int, int, float*, float*,
                          hipStream_t);
 size_t align_workspace_bytes(int T, int K1, int E1);
@@ -26,7 +30,7 @@ hipError_t launch_combine(const uint16_t*, const uint16_t*, int, int, int, uint1
 hipError_t launch_gate_up_decode(const uint8_t*, const float*, const uint8_t*, const float*, bool,
                                  const int32_t*, const int32_t*, float*, int, int, int, int, int,
                                  hipStream_t);
-hipError_t launch_layer_front(const float*, int, int, int, float, int32_t*, float*, const uint16_t*,
+hipError_t launch_layer_front(const LogitSrc&, int, int, int, float, int32_t*, float*, const uint16_t*,
                               int, bool, uint8_t*, float*, hipStream_t);
 bool expert_ffn_decode_supported(int H, int I);
 bool expert_ffn_decode_align_supported(int T, int K1);
@@ -156,7 +160,8 @@ int moe_route_topk_plus_shared(const float* logits, int T, int E, int K, float s
   if (T == 0) return SRMOE_OK;
   if (!logits || !topk_ids || !topk_w) return SRMOE_ERR_INVALID_ARG;
   if (!aligned16(logits) || !aligned16(topk_ids) || !aligned16(topk_w)) return SRMOE_ERR_INVALID_ARG;
-  return hip_status(launch_route(logits, T, E, K, shared_weight, topk_ids, topk_w, as_stream(stream)));
+  return hip_status(launch_route(LogitSrc{logits, nullptr, 0, 0}, T, E, K, shared_weight, topk_ids, topk_w,
+                                  as_stream(stream)));
 }
 
 size_t moe_router_workspace_bytes(int T, int H, int E) {
@@ -343,13 +348,13 @@ int moe_fused_ffn(const uint16_t* x, const uint8_t* w13, const float* s13, const
                          block_expert, num_padded, topk_w, workspace, ws_bytes, stream);
 }
 
-int moe_layer_forward(const uint16_t* x, const float* logits, const uint8_t* w13, const float* s13,
+static int layer_forward(const uint16_t* x, const LogitSrc& src, const void* logits, const uint8_t* w13, const float* s13,
                       const uint8_t* w2, const float* s2, int scale_mode, int T, int H, int I, int E,
                       int K, float shared_weight, int block_m, int32_t* topk_ids, float* topk_w,
                       int32_t* sorted_slot_ids, int32_t* block_expert, int32_t* expert_counts,
                       int32_t* expert_offsets, int32_t* num_padded, void* align_ws,
                       size_t align_ws_bytes, void* ffn_ws, size_t ffn_ws_bytes, uint16_t* out,
-                      void* stream) {
+                      void* stream, const std::function<int(LogitSrc*, hipStream_t)>& gate) {
   // every check of the four calls, before anything is launched
   if (T < 0 || T > kMaxT || E < 1 || K < 0) return SRMOE_ERR_INVALID_ARG;
   if (E > 255 || K > E || K > 15) return SRMOE_ERR_UNSUPPORTED;
@@ -367,7 +372,12 @@ int moe_layer_forward(const uint16_t* x, const float* logits, const uint8_t* w13
   char* ws = static_cast<char*>(ffn_ws);
   const bool blk = scale_mode == SRMOE_SCALE_BLOCK128;
   hipStream_t sm = as_stream(stream);
-  st = hip_status(launch_layer_front(logits, T, E, K, shared_weight, topk_ids, topk_w, x, H, blk,
+  LogitSrc lsrc = src;
+  if (gate) {
+    st = gate(&lsrc, sm);
+    if (st != SRMOE_OK) return st;
+  }
+  st = hip_status(launch_layer_front(lsrc, T, E, K, shared_weight, topk_ids, topk_w, x, H, blk,
                                      reinterpret_cast<uint8_t*>(ws + L.xq),
                                      reinterpret_cast<float*>(ws + L.sx), sm));
   if (st != SRMOE_OK) return st;
@@ -390,6 +400,87 @@ int moe_layer_forward(const uint16_t* x, const float* logits, const uint8_t* w13
                        block_expert, num_padded, topk_w, ffn_ws, ffn_ws_bytes, stream);
   if (st != SRMOE_OK) return st;
   return moe_combine(T, K1, H, ffn_ws, ffn_ws_bytes, out, stream);
+}
+
+int moe_layer_forward(const uint16_t* x, const float* logits, const uint8_t* w13, const float* s13,
+                      const uint8_t* w2, const float* s2, int scale_mode, int T, int H, int I, int E,
+                      int K, float shared_weight, int block_m, int32_t* topk_ids, float* topk_w,
+                      int32_t* sorted_slot_ids, int32_t* block_expert, int32_t* expert_counts,
+                      int32_t* expert_offsets, int32_t* num_padded, void* align_ws,
+                      size_t align_ws_bytes, void* ffn_ws, size_t ffn_ws_bytes, uint16_t* out,
+                      void* stream) {
+  return layer_forward(x, LogitSrc{logits, nullptr, 0, 0}, logits, w13, s13, w2, s2, scale_mode, T, H, I, E, K,
+                       shared_weight, block_m, topk_ids, topk_w, sorted_slot_ids, block_expert,
+                       expert_counts, expert_offsets, num_padded, align_ws, align_ws_bytes, ffn_ws,
+                       ffn_ws_bytes, out, stream, nullptr);
+}
+
+size_t moe_route_from_x_workspace_bytes(int T, int H, int E) {
+  if (T <= 0 || H <= 0 || E < 1) return 0;
+  const int ks = router_splits(T, H, E);
+  return (size_t)(ks > 1 ? ks : 1) * T * E * sizeof(float);
+}
+
+// Router gate into the workspace (partial tiles, or the logits themselves when the gate
+// runs in one K chunk); the routing kernels then read it through a LogitSrc.
+static int router_into(const uint16_t* x, const float* w_router, const float* bias, int T, int H, int E,
+                       void* ws, LogitSrc* src, hipStream_t sm) {
+  float* dst = static_cast<float*>(ws);
+  const int ks = router_splits(T, H, E);
+  const int st = hip_status(launch_router_gemm(x, w_router, bias, T, H, E, dst, sm));
+  *src = ks > 1 ? LogitSrc{dst, bias, ks, (size_t)T * E} : LogitSrc{dst, nullptr, 0, 0};
+  return st;
+}
+
+static int check_router_args(const uint16_t* x, const float* w_router, const float* bias, int T, int H,
+                             int E, const void* ws, size_t ws_bytes) {
+  if (H <= 0) return SRMOE_ERR_INVALID_ARG;
+  if (H % 128 != 0) return SRMOE_ERR_UNSUPPORTED;
+  if (T == 0) return SRMOE_OK;
+  if (!x || !w_router || !ws || !aligned16(x) || !aligned16(w_router) || !aligned16(ws) ||
+      (bias && !aligned16(bias)))
+    return SRMOE_ERR_INVALID_ARG;
+  if (ws_bytes < moe_route_from_x_workspace_bytes(T, H, E)) return SRMOE_ERR_WORKSPACE;
+  return SRMOE_OK;
+}
+
+int moe_route_from_x(const uint16_t* x, const float* w_router, const float* bias, int T, int H, int E, int K,
+                     float shared_weight, int32_t* topk_ids, float* topk_w, void* workspace, size_t ws_bytes,
+                     void* stream) {
+  if (T < 0 || T > kMaxT || E < 1 || K < 0) return SRMOE_ERR_INVALID_ARG;
+  if (E > 255 || K > E || K > 15) return SRMOE_ERR_UNSUPPORTED;
+  int st = check_router_args(x, w_router, bias, T, H, E, workspace, ws_bytes);
+  if (st != SRMOE_OK || T == 0) return st;
+  if (!topk_ids || !topk_w || !aligned16(topk_ids) || !aligned16(topk_w)) return SRMOE_ERR_INVALID_ARG;
+  hipStream_t sm = as_stream(stream);
+  LogitSrc src;
+  st = router_into(x, w_router, bias, T, H, E, workspace, &src, sm);
+  if (st != SRMOE_OK) return st;
+  return hip_status(launch_route(src, T, E, K, shared_weight, topk_ids, topk_w, sm));
+}
+
+int moe_layer_forward_from_x(const uint16_t* x, const float* w_router, const float* bias,
+                             const uint8_t* w13, const float* s13, const uint8_t* w2, const float* s2,
+                             int scale_mode, int T, int H, int I, int E, int K, float shared_weight,
+                             int block_m, int32_t* topk_ids, float* topk_w, int32_t* sorted_slot_ids,
+                             int32_t* block_expert, int32_t* expert_counts, int32_t* expert_offsets,
+                             int32_t* num_padded, void* router_ws, size_t router_ws_bytes, void* align_ws,
+                             size_t align_ws_bytes, void* ffn_ws, size_t ffn_ws_bytes, uint16_t* out,
+                             void* stream) {
+  // the shape checks of the layer first, then the gate's
+  if (T < 0 || T > kMaxT || E < 1 || K < 0) return SRMOE_ERR_INVALID_ARG;
+  if (E > 255 || K > E || K > 15) return SRMOE_ERR_UNSUPPORTED;
+  int st = check_ffn_dims(scale_mode, T, H, I, E + 1, K + 1, block_m);
+  if (st != SRMOE_OK) return st;
+  st = check_router_args(x, w_router, bias, T, H, E, router_ws, router_ws_bytes);
+  if (st != SRMOE_OK) return st;
+  // a stand-in for the logits pointer, so that the layer's own checks pass before the gate runs
+  return layer_forward(x, LogitSrc{nullptr, nullptr, 0, 0}, router_ws, w13, s13, w2, s2, scale_mode, T, H, I,
+                       E, K, shared_weight, block_m, topk_ids, topk_w, sorted_slot_ids, block_expert,
+                       expert_counts, expert_offsets, num_padded, align_ws, align_ws_bytes, ffn_ws,
+                       ffn_ws_bytes, out, stream, [&](LogitSrc* src, hipStream_t sm) {
+                         return router_into(x, w_router, bias, T, H, E, router_ws, src, sm);
+                       });
 }
 
 int moe_combine(int T, int K1, int H, const void* workspace, size_t ws_bytes, uint16_t* out,

@@ -109,7 +109,7 @@ __global__ void __launch_bounds__(512) expert_ffn_decode_kernel(
   const int b = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar loop control
-  const int r16 = lane & 15, kq = lane >> 4, r8 = lane >> 3;
+  const int r16 = lane & 15, kq = lane >> 4;
   const int sentinel = T * K1;
   const uint64_t magic = slot_div_magic(K1);
   const int HB = H / kGroup, nsteps = H / kGroup;

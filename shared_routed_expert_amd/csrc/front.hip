@@ -11,7 +11,7 @@ namespace srmoe {
 
 template <bool kBlock>
 __global__ void __launch_bounds__(256) layer_front_kernel(
-    const float* __restrict__ logits, int T, int E, int K, float shared_weight,
+    const LogitSrc logits, int T, int E, int K, float shared_weight,
     int32_t* __restrict__ ids, float* __restrict__ w, const uint16_t* __restrict__ x, int H,
     uint8_t* __restrict__ xq, float* __restrict__ sx) {
   __shared__ float red[4];
@@ -24,7 +24,7 @@ __global__ void __launch_bounds__(256) layer_front_kernel(
   quant_x_token<kBlock>(x, blockIdx.x - route_blocks, true, H, xq, sx, threadIdx.x, red);
 }
 
-hipError_t launch_layer_front(const float* logits, int T, int E, int K, float shared_weight,
+hipError_t launch_layer_front(const LogitSrc& logits, int T, int E, int K, float shared_weight,
                               int32_t* ids, float* w, const uint16_t* x, int H, bool block,
                               uint8_t* xq, float* sx, hipStream_t stream) {
   const dim3 grid((T + 3) / 4 + T);

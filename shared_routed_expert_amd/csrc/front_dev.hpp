@@ -16,6 +16,32 @@ __device__ __forceinline__ float key_to_float(uint32_t k) {
   return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
 }
 
+// Where the router logits of a token come from: a [T,E] float32 array (ks == 0), or the
+// router gate's K-split partial tiles part[c][T][E], c < ks, summed in chunk order and
+// then offset by the bias -- the same float32 operations, in the same order, as the
+// gate's own reduction pass, so both give the same logits bit for bit.
+struct LogitSrc {
+  const float* p;
+  const float* bias;   // with ks > 0 (may be null)
+  int ks;
+  size_t stride;       // T * E: distance between partial tiles
+};
+__device__ __forceinline__ float logit_at(const LogitSrc& s, int t, int E, int e) {
+  const size_t i = (size_t)t * E + e;
+  if (s.ks == 0) return s.p[i];
+  // 16 partial loads in flight at a time, summed in chunk order
+  float v = 0.f;
+  for (int c0 = 0; c0 < s.ks; c0 += 16) {
+    float t[16];
+#pragma unroll
+    for (int c = 0; c < 16; ++c) t[c] = c0 + c < s.ks ? s.p[(size_t)(c0 + c) * s.stride + i] : 0.f;
+#pragma unroll
+    for (int c = 0; c < 16; ++c)
+      if (c0 + c < s.ks) v += t[c];
+  }
+  return v + (s.bias ? s.bias[e] : 0.f);
+}
+
 // Route token t with the 64 lanes of the caller's wavefront: the K routed experts
 // with the largest logits in the order (logit desc, id asc), weights
 // p_k / sum_{j in top-K} p_j (the full softmax denominator cancels; exponents are
@@ -25,7 +51,7 @@ __device__ __forceinline__ float key_to_float(uint32_t k) {
 // 64-bit key (ordered logit, 255 - id). ids/w are written to global memory;
 // lds_ids (if not null) gets a copy of the ids. With append_shared false the rows
 // have K entries and no shared slot (the routed-only router of the unfused layer).
-__device__ __forceinline__ void route_token_wave(const float* __restrict__ logits, int t, int E, int K,
+__device__ __forceinline__ void route_token_wave(const LogitSrc& logits, int t, int E, int K,
                                                  float shared_weight, int32_t* __restrict__ ids,
                                                  float* __restrict__ w, int* lds_ids,
                                                  bool append_shared = true) {
@@ -35,7 +61,7 @@ __device__ __forceinline__ void route_token_wave(const float* __restrict__ logit
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int e = lane + 64 * j;
-    key[j] = (e < E) ? ((uint64_t)ordered_key(logits[(size_t)t * E + e]) << 32) | (uint32_t)(255 - e)
+    key[j] = (e < E) ? ((uint64_t)ordered_key(logit_at(logits, t, E, e)) << 32) | (uint32_t)(255 - e)
                      : 0ull;
   }
   int sel_id[15];

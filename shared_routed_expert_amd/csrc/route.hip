@@ -10,7 +10,7 @@
 namespace srmoe {
 
 __global__ void __launch_bounds__(256) route_topk_plus_shared_kernel(
-    const float* __restrict__ logits, int T, int E, int K, float shared_weight,
+    const LogitSrc logits, int T, int E, int K, float shared_weight,
     int32_t* __restrict__ ids, float* __restrict__ w) {
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;   // whole wavefronts leave together
@@ -24,10 +24,10 @@ __global__ void __launch_bounds__(256) route_topk_kernel(const float* __restrict
                                                          float* __restrict__ w) {
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
-  route_token_wave(logits, t, E, K, 0.f, ids, w, nullptr, false);
+  route_token_wave(LogitSrc{logits, nullptr, 0, 0}, t, E, K, 0.f, ids, w, nullptr, false);
 }
 
-hipError_t launch_route(const float* logits, int T, int E, int K, float shared_weight, int32_t* ids,
+hipError_t launch_route(const LogitSrc& logits, int T, int E, int K, float shared_weight, int32_t* ids,
                         float* w, hipStream_t stream) {
   hipLaunchKernelGGL(route_topk_plus_shared_kernel, dim3((T + 3) / 4), dim3(256), 0, stream, logits,
                      T, E, K, shared_weight, ids, w);

@@ -180,11 +180,15 @@ size_t router_workspace_bytes(int T, int H, int E) {
   return p.ks > 1 ? (size_t)p.ks * T * E * sizeof(float) : 0;
 }
 
-hipError_t launch_router(const uint16_t* x, const float* w, const float* bias, int T, int H, int E,
-                         float* logits, float* part, hipStream_t stream) {
+int router_splits(int T, int H, int E) { return router_plan(T, H, E).ks; }
+
+// The GEMM pass alone: with one K chunk it writes the logits (bias included) to dst,
+// otherwise the partial tiles [ks][T][E] (summed by router_reduce_kernel, or by the
+// routing kernels through LogitSrc).
+hipError_t launch_router_gemm(const uint16_t* x, const float* w, const float* bias, int T, int H, int E,
+                              float* dst, hipStream_t stream) {
   const RouterPlan p = router_plan(T, H, E);
   const int direct = p.ks == 1;
-  float* dst = direct ? logits : part;
   const dim3 grid((T + 64 * p.mt - 1) / (64 * p.mt), (E + kRExp - 1) / kRExp, p.ks);
   // H % 128 == 0, so a 256-element chunk is whole except possibly the last one of H % 256 == 128:
   // that one runs the streaming kernel
@@ -197,7 +201,15 @@ hipError_t launch_router(const uint16_t* x, const float* w, const float* bias, i
   else
     hipLaunchKernelGGL((router_gemm_kernel<4, 0>), grid, dim3(256), 0, stream, x, w, bias, T, H, E,
                        p.kchunk, direct, dst);
-  if (direct) return hipGetLastError();
+  return hipGetLastError();
+}
+
+hipError_t launch_router(const uint16_t* x, const float* w, const float* bias, int T, int H, int E,
+                         float* logits, float* part, hipStream_t stream) {
+  const RouterPlan p = router_plan(T, H, E);
+  if (p.ks == 1) return launch_router_gemm(x, w, bias, T, H, E, logits, stream);
+  const hipError_t e = launch_router_gemm(x, w, bias, T, H, E, part, stream);
+  if (e != hipSuccess) return e;
   const size_t n = (size_t)T * E;
   hipLaunchKernelGGL(router_reduce_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream,
                      part, bias, T, E, p.ks, logits);

@@ -123,6 +123,20 @@ class FusedMoE:
                             self.align_ws, self.align_ws_bytes, self.ws, self.ws_bytes, self.out, stream)
         return self.out
 
+    def forward_from_x(self, x, w_router, bias, W: DeviceWeights, shared_weight=1.0, stream=None):
+        """The layer from x and the router weight (moe_layer_forward_from_x: the router gate
+        in front, its partial sums folded into the routing)."""
+        T, H, I, E1, K1, bm = self.dims()
+        if not hasattr(self, "router_ws"):
+            self.router_ws_bytes = L.moe_route_from_x_workspace_bytes(T, H, self.E)
+            self.router_ws = torch.empty(max(self.router_ws_bytes, 16), dtype=torch.uint8, device=self.out.device)
+        L.moe_layer_forward_from_x(x, w_router, bias, W.w13, W.s13, W.w2, W.s2, self.scale_mode, T, H, I, self.E,
+                                   self.K, shared_weight, bm, self.topk_ids, self.topk_w, self.sorted_slot_ids,
+                                   self.block_expert, self.expert_counts, self.expert_offsets, self.num_padded,
+                                   self.router_ws, self.router_ws_bytes, self.align_ws, self.align_ws_bytes,
+                                   self.ws, self.ws_bytes, self.out, stream)
+        return self.out
+
     # views into the workspace, for inspecting the stages
     def ws_view(self, name, dtype, shape):
         off = self.offsets[name]

@@ -286,3 +286,40 @@ def test_rope_table_rejects(L):
     assert f(FAKE, 0, 64, 1e6) == -1 and f(FAKE, 16, 63, 1e6) == -1 and f(FAKE, 16, 64, 1.0) == -1
     assert f(None, 16, 64, 1e6) == -1 and f(MIS, 16, 64, 1e6) == -1
     assert f(FAKE, 1 << 26, 64, 1e6) == -2
+
+
+def test_route_from_x_rejects(L):
+    wsb = L.moe_route_from_x_workspace_bytes(64, 5120, 160)
+    assert wsb >= 64 * 160 * 4 and L.moe_route_from_x_workspace_bytes(0, 5120, 160) == 0
+    f = lambda **kw: L.moe_route_from_x(**{**dict(x=FAKE, w_router=FAKE, bias=None, T=64, H=5120, E=160, K=8,
+                                                   shared_weight=1.0, topk_ids=FAKE, topk_w=FAKE, workspace=FAKE,
+                                                   ws_bytes=wsb), **kw}, stream=0, check=False)
+    assert f(T=-1) == -1 and f(E=0) == -1 and f(K=-1) == -1 and f(H=0) == -1
+    assert f(E=256) == -2 and f(K=16) == -2 and f(H=5000) == -2
+    for name in ("x", "w_router", "topk_ids", "topk_w", "workspace"):
+        assert f(**{name: None}) == -1, name
+        assert f(**{name: MIS}) == -1, name
+    assert f(bias=MIS) == -1
+    assert f(ws_bytes=wsb - 1) == -3
+    assert f(T=0, x=None, topk_ids=None) == 0
+
+
+def test_layer_forward_from_x_rejects(L):
+    T, H, I, E, K, bm = 64, 5120, 192, 160, 8, 16
+    rwb = L.moe_route_from_x_workspace_bytes(T, H, E)
+    awb = L.moe_align_workspace_bytes(T, K + 1, E + 1)
+    fwb = L.moe_ffn_workspace_bytes(T, H, I, E + 1, K + 1, bm, 0)
+
+    def f(**kw):
+        a = dict(x=FAKE, w_router=FAKE, bias=None, w13=FAKE, s13=FAKE, w2=FAKE, s2=FAKE, scale_mode=0, T=T, H=H,
+                 I=I, E=E, K=K, shared_weight=1.0, block_m=bm, topk_ids=FAKE, topk_w=FAKE, sorted_slot_ids=FAKE,
+                 block_expert=FAKE, expert_counts=FAKE, expert_offsets=FAKE, num_padded=FAKE, router_ws=FAKE,
+                 router_ws_bytes=rwb, align_ws=FAKE, align_ws_bytes=awb, ffn_ws=FAKE, ffn_ws_bytes=fwb, out=FAKE)
+        a.update(kw)
+        return L.moe_layer_forward_from_x(**a, stream=0, check=False)
+    assert f(T=-1) == -1 and f(E=0) == -1 and f(H=0) == -1
+    assert f(E=256) == -2 and f(I=100) == -2 and f(block_m=48) == -2
+    for name in ("x", "w_router", "w13", "out", "router_ws", "ffn_ws", "topk_ids"):
+        assert f(**{name: None}) == -1, name
+    assert f(router_ws_bytes=rwb - 1) == -3 and f(ffn_ws_bytes=fwb - 1) == -3 and f(align_ws_bytes=awb - 1) == -3
+    assert f(T=0, x=None, out=None) == 0
