@@ -153,7 +153,8 @@ __global__ void __launch_bounds__(256) router_reduce_kernel(const float* __restr
 
 // Small batches (T <= 256): one 16-token fragment per wavefront and K chunks of 256
 // (8 steps, all loads up front). Larger: four fragments per wavefront (each split
-// weight fragment feeds four token tiles) and enough K chunks for ~256 workgroups.
+// weight fragment feeds four token tiles) and K split so that the workgroups spread
+// evenly over the CUs.
 constexpr int kRSmallT = 256;
 struct RouterPlan {
   int mt, ks, kchunk;
@@ -165,10 +166,25 @@ static RouterPlan router_plan(int T, int H, int E) {
     p.kchunk = 256;
   } else {
     p.mt = 4;
+    // K splits: the smallest k minimising ceil(tiles k / 256) / k, the number of workgroups
+    // each of the 256 CUs runs times the work of one (a split count that leaves a few CUs
+    // with one workgroup more than the rest costs a whole extra round)
     const int tiles = ((T + 255) / 256) * ((E + kRExp - 1) / kRExp);
-    int k = 256 / tiles;
-    k = k > H / 256 ? H / 256 : k;
-    k = k < 1 ? 1 : k;
+    // (at most 8 splits, or as many as fill the GPU with one round when the tiles are few;
+    // each split adds a [T, E] float32 partial tile to write and sum)
+    int kmax = 256 / tiles > 8 ? 256 / tiles : 8;
+    kmax = kmax > H / 256 ? H / 256 : kmax;
+    kmax = kmax < 1 ? 1 : kmax;
+    int k = 1;
+    long best_num = (tiles + 255) / 256, best_den = 1;
+    for (int c = 2; c <= kmax; ++c) {
+      const long num = ((long)tiles * c + 255) / 256;
+      if (num * best_den < best_num * c) {
+        best_num = num;
+        best_den = c;
+        k = c;
+      }
+    }
     p.kchunk = ((H + k - 1) / k + 31) / 32 * 32;
   }
   p.ks = (H + p.kchunk - 1) / p.kchunk;
