@@ -8,8 +8,11 @@ decode shard: T=64 tokens, H=5120, 160 routed + 1 shared experts, I=192,
 top-8 + shared. Two independent weight sets (2 x 475 MB) are cycled so the
 weights stream from HBM rather than from the 256 MB last-level cache.
 
-Prints one JSON line (see README/DESIGN for the fields). `--gpus` above 1 is
-refused: this build measures one GPU.
+Prints one JSON line: the layer's tokens/s and time per step, the roofline of the
+dominant expert kernel (its algorithmic bytes over its measured launch time, against
+8 TB/s), per-stage times, the router gate, the layer from x, the QK-Norm + RoPE step,
+the fused-vs-unfused comparison and the CPU oracle's rate. `--gpus` above 1 is
+refused: the library runs on one GPU.
 """
 from __future__ import annotations
 
@@ -293,8 +296,9 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(see DESIGN.md, 'How the path would shard').", file=sys.stderr)
+        print("bench.py measures one GPU only: the library has no multi-GPU path (under TP8 each GPU "
+              "runs this layer on its 192-wide slice of every expert and an all-reduce sums the "
+              "partial outputs; that exchange is not built).", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
