@@ -348,6 +348,18 @@ def main():
     ms_per_step = ev0.elapsed_time(ev1) / args.steps
     log(f"bench: {ms_per_step * 1e3:.1f} us/step on the GPU, {wall * 1e6 / args.steps:.1f} us/step wall-clock")
 
+    # Per-step durations of the same layer call (events around each step), for the
+    # median and the 10th / 90th percentiles.
+    sev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    torch.cuda.synchronize()
+    sev[0].record(stream)
+    for i in range(args.steps):
+        step(i)
+        sev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    step_us = sorted(1e3 * sev[i].elapsed_time(sev[i + 1]) for i in range(args.steps))
+    pct = lambda q: step_us[min(len(step_us) - 1, int(q * (len(step_us) - 1) + 0.5))]
+
     # The same K steps through the four separate calls, for comparison.
     torch.cuda.synchronize()
     ev0.record(stream)
@@ -425,6 +437,9 @@ def main():
                   "hbm_frac": round(layer_bytes / step_s / 1e9 / HBM_PEAK_GBS, 4),
                   "alg_TFLOPs": round(flops / step_s / 1e12, 2),
                   "fp8_frac": round(flops / step_s / 1e12 / FP8_PEAK_TFLOPS, 4),
+                  "roofline_frac": round(max(flops / (FP8_PEAK_TFLOPS * 1e12), layer_bytes / (HBM_PEAK_GBS * 1e9))
+                                         / (pct(0.5) * 1e-6), 4),
+                  "step_us_p10_p50_p90": [round(pct(0.1), 2), round(pct(0.5), 2), round(pct(0.9), 2)],
                   "stage_us": {k: round(v, 2) for k, v in stage_us.items()},
                   "entry_point": "moe_layer_forward",
                   "four_call_ms_per_step": round(four_ms, 5)},
