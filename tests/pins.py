@@ -295,3 +295,107 @@ def check_permutation_equivariance(moe_fused, inp, perm):
     a = moe_fused(x, inp.logits, K, inp.w13_q, inp.s13, inp.w2_q, inp.s2)
     b = moe_fused(x[perm], inp.logits[perm], K, inp.w13_q, inp.s13, inp.w2_q, inp.s2)
     _require(np.allclose(a[perm], b, rtol=0, atol=1e-12 * np.abs(a).max()), "token permutation")
+
+
+# ----------------------------------------------------------------------------- router gate
+def check_router_bruteforce(router_logits):
+    """Pure-Python triple loop on tiny inputs (no numpy matmul), bias included."""
+    rng = np.random.default_rng(5)
+    x = rng.standard_normal((3, 7)).astype(np.float32)
+    w = rng.standard_normal((4, 7)).astype(np.float32)
+    b = rng.standard_normal(4).astype(np.float32)
+    got = router_logits(x, w, b)
+    for t in range(3):
+        for e in range(4):
+            acc = float(b[e])
+            for h in range(7):
+                acc += float(x[t, h]) * float(w[e, h])
+            _require(abs(got[t, e] - acc) <= 1e-12 * (1 + abs(acc)), f"router logit ({t},{e})")
+
+
+def check_router_one_hot(router_logits):
+    """x = unit vectors: the logits are the router weight's columns (plus the bias), exactly."""
+    rng = np.random.default_rng(6)
+    w = rng.standard_normal((5, 8)).astype(np.float32)
+    b = rng.standard_normal(5).astype(np.float32)
+    got = router_logits(np.eye(8, dtype=np.float32), w, b)
+    _require(np.array_equal(got, w.T.astype(np.float64) + b.astype(np.float64)[None, :]), "one-hot rows + bias")
+    _require(np.array_equal(router_logits(np.eye(8, dtype=np.float32), w), w.T.astype(np.float64)),
+             "one-hot rows")
+
+
+# ----------------------------------------------------------------------------- QK-Norm + RoPE
+def check_head_rms_norm(head_rms_norm):
+    # a constant head c: every entry becomes sign(c) / sqrt(1 + eps / c^2) * w
+    w = np.linspace(0.5, 1.5, 8)
+    got = head_rms_norm(np.full((1, 8), -3.0), w, 1e-6)
+    _require(np.allclose(got, -w / np.sqrt(1 + 1e-6 / 9.0), rtol=0, atol=1e-15), "constant head")
+    # unit weight, eps 0: mean square exactly 1 (up to rounding); scale invariance
+    x = np.random.default_rng(1).standard_normal((5, 3, 16))
+    y = head_rms_norm(x, np.ones(16), 0.0)
+    _require(np.allclose(np.mean(y * y, axis=-1), 1.0, atol=1e-14), "unit mean square")
+    _require(np.allclose(head_rms_norm(7.5 * x, np.ones(16), 0.0), y, atol=1e-14), "scale invariance")
+
+
+def check_rope_angles(rope_angles):
+    # hand values: theta = 100, rotary_dim = 4 -> frequencies 100^0 = 1 and 100^(-1/2) = 1/10
+    got = rope_angles(np.array([0, 10, 30]), 4, 100.0)
+    _require(np.allclose(got, [[0.0, 0.0], [10.0, 1.0], [30.0, 3.0]], rtol=0, atol=1e-12), "angles")
+
+
+def check_rope_half(rope_half, rope_angles):
+    rng = np.random.default_rng(2)
+    x = rng.standard_normal((4, 2, 16))
+    rd, h = 8, 4
+    _require(np.array_equal(rope_half(x, rope_angles(np.zeros(4), rd, 10000.0), rd), x), "position 0")
+    pos = np.array([1, 5, 17, 1000])
+    y = rope_half(x, rope_angles(pos, rd, 10000.0), rd)
+    _require(np.array_equal(y[..., rd:], x[..., rd:]), "dims past rotary_dim pass through")
+    _require(np.allclose(y[..., :h] ** 2 + y[..., h:rd] ** 2, x[..., :h] ** 2 + x[..., h:rd] ** 2, atol=1e-12),
+             "pair lengths")
+    q = np.array([3, 4, 5, 6])
+    _require(np.allclose(rope_half(y, rope_angles(q, rd, 10000.0), rd),
+                         rope_half(x, rope_angles(pos + q, rd, 10000.0), rd), atol=1e-10), "composition")
+    # pair 0 (dims 0 and h) at position p is (x0 + i x_h) e^{i p}
+    z = (x[:, :, 0] + 1j * x[:, :, h]) * np.exp(1j * pos.astype(np.float64))[:, None]
+    _require(np.allclose(y[:, :, 0], z.real, atol=1e-12) and np.allclose(y[:, :, h], z.imag, atol=1e-12),
+             "pair 0")
+    # pair 1 (dims 1 and h + 1) with theta = 100, rd = 8 turns by p * 100^(-1/4) = p / sqrt(10)
+    y2 = rope_half(x[:1], rope_angles(np.array([10]), rd, 100.0), rd)
+    z1 = (x[0, :, 1] + 1j * x[0, :, h + 1]) * np.exp(1j * 10.0 / math.sqrt(10.0))
+    _require(np.allclose(y2[0, :, 1], z1.real, atol=1e-12) and np.allclose(y2[0, :, h + 1], z1.imag, atol=1e-12),
+             "pair 1")
+
+
+def check_rope_interleaved(rope_interleaved, rope_half, rope_angles):
+    """Interleaved pairs (2i, 2i+1) are rotate-half pairs (i, i + rd/2) once the even dims
+    are moved to the front; position 0 leaves x as it is; pair 0 is a complex product."""
+    rng = np.random.default_rng(4)
+    D, rd = 16, 8
+    x = rng.standard_normal((3, 2, D))
+    pos = np.array([0.0, 7.0, 123.0])
+    ang = rope_angles(pos, rd, 500.0)
+    perm = np.concatenate([np.arange(0, rd, 2), np.arange(1, rd, 2), np.arange(rd, D)])
+    via_half = rope_half(x[..., perm], ang, rd)[..., np.argsort(perm)]
+    y = rope_interleaved(x, ang, rd)
+    _require(np.allclose(y, via_half, atol=1e-13), "permuted rotate-half")
+    _require(np.array_equal(rope_interleaved(x[:1], ang[:1], rd), x[:1]), "position 0")
+    z = (x[:, :, 0] + 1j * x[:, :, 1]) * np.exp(1j * pos)[:, None]
+    _require(np.allclose(y[:, :, 0], z.real, atol=1e-12) and np.allclose(y[:, :, 1], z.imag, atol=1e-12), "pair 0")
+    _require(np.array_equal(y[..., rd:], x[..., rd:]), "dims past rotary_dim pass through")
+
+
+def check_qk_layout(qk_norm_rope, head_rms_norm):
+    """q and k heads are normalised with their own weights and rotated; v passes through."""
+    rng = np.random.default_rng(3)
+    T, Hq, Hkv, D, rd = 3, 2, 1, 8, 4
+    qkv = rng.standard_normal((T, (Hq + 2 * Hkv) * D))
+    qw, kw = rng.uniform(0.5, 1.5, D), rng.uniform(0.5, 1.5, D)
+    out = qk_norm_rope(qkv, Hq, Hkv, D, rd, qw, kw, 1e-6, np.array([0, 2, 9]), 10000.0)
+    heads_in = qkv.reshape(T, Hq + 2 * Hkv, D)
+    heads = out.reshape(T, Hq + 2 * Hkv, D)
+    _require(np.array_equal(heads[:, Hq + Hkv:], heads_in[:, Hq + Hkv:]), "v heads untouched")
+    _require(np.allclose(heads[0, :Hq], head_rms_norm(heads_in[0, :Hq], qw, 1e-6)), "q at position 0")
+    _require(np.allclose(heads[0, Hq], head_rms_norm(heads_in[0, Hq], kw, 1e-6)), "k at position 0")
+    _require(np.allclose(heads[:, :Hq, rd:], head_rms_norm(heads_in[:, :Hq], qw, 1e-6)[..., rd:]),
+             "dims past rotary_dim are the normalised values")

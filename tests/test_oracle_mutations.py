@@ -169,3 +169,84 @@ def test_mut_combine_drops_shared_slot(monkeypatch, tiny):
     monkeypatch.setattr(om, "combine_slots", _mut_combine_drop_last)
     _fails(pins.check_fused_equals_unfused, om.moe_fused, om.moe_unfused, tiny)
     _fails(pins.check_zero_routed_is_dense_shared, om.moe_fused, om.combine_slots, om.dense_shared_ffn, tiny)
+
+
+# ----------------------------------------------------------------------------- router gate
+def _router_no_bias(x, w, bias=None):
+    return np.asarray(x, np.float64) @ np.asarray(w, np.float64).T
+
+
+def _router_fp32(x, w, bias=None):
+    out = np.asarray(x, np.float32) @ np.asarray(w, np.float32).T
+    return (out + (0 if bias is None else np.asarray(bias, np.float32))).astype(np.float64)
+
+
+def test_mut_router_drops_bias():
+    _fails(pins.check_router_bruteforce, _router_no_bias)
+    _fails(pins.check_router_one_hot, _router_no_bias)
+
+
+def test_mut_router_float32_sums():
+    _fails(pins.check_router_bruteforce, _router_fp32)
+
+
+# ----------------------------------------------------------------------------- QK-Norm + RoPE
+from oracle import attn as oa   # noqa: E402
+
+
+def _norm_no_eps(x, w, eps):
+    x = np.asarray(x, np.float64)
+    return x / np.sqrt(np.mean(x * x, axis=-1, keepdims=True)) * w
+
+
+def _norm_mean_abs(x, w, eps):
+    x = np.asarray(x, np.float64)
+    return x / (np.mean(np.abs(x), axis=-1, keepdims=True) + eps) * w
+
+
+def _angles_wrong_exponent(positions, rd, theta):
+    i = np.arange(rd // 2, dtype=np.float64)
+    return np.asarray(positions, np.float64)[:, None] * (theta ** (-i / rd))[None, :]
+
+
+def _rope_reversed(x, angle, rd):
+    return oa.rope_half(x, -np.asarray(angle), rd)
+
+
+def _rope_adjacent_pairs(x, angle, rd):
+    return oa.rope_interleaved(x, angle, rd)
+
+
+def _qk_norms_v_too(qkv, Hq, Hkv, D, rd, qw, kw, eps, positions, theta, neox=True):
+    out = oa.qk_norm_rope(qkv, Hq, Hkv, D, rd, qw, kw, eps, positions, theta, neox).reshape(qkv.shape[0], -1, D)
+    v = out[:, Hq + Hkv:]
+    out[:, Hq + Hkv:] = oa.head_rms_norm(v, kw, eps)
+    return out.reshape(qkv.shape[0], -1)
+
+
+def _qk_k_weight_for_q(qkv, Hq, Hkv, D, rd, qw, kw, eps, positions, theta, neox=True):
+    return oa.qk_norm_rope(qkv, Hq, Hkv, D, rd, kw, kw, eps, positions, theta, neox)
+
+
+@pytest.mark.parametrize("mut", [_norm_no_eps, _norm_mean_abs])
+def test_mut_head_norm(mut):
+    _fails(pins.check_head_rms_norm, mut)
+
+
+def test_mut_rope_frequency_exponent():
+    _fails(pins.check_rope_angles, _angles_wrong_exponent)
+    _fails(pins.check_rope_half, oa.rope_half, _angles_wrong_exponent)
+
+
+@pytest.mark.parametrize("mut", [_rope_reversed, _rope_adjacent_pairs])
+def test_mut_rope_rotation(mut):
+    _fails(pins.check_rope_half, mut, oa.rope_angles)
+
+
+def test_mut_rope_interleaved_as_rotate_half():
+    _fails(pins.check_rope_interleaved, oa.rope_half, oa.rope_half, oa.rope_angles)
+
+
+@pytest.mark.parametrize("mut", [_qk_norms_v_too, _qk_k_weight_for_q])
+def test_mut_qk_layout(mut):
+    _fails(pins.check_qk_layout, mut, oa.head_rms_norm)

@@ -203,28 +203,11 @@ def test_fp32_masters_close_to_fp8(tiny):
 
 # ---------------------------------------------------------------------------- router gate
 def test_router_logits_bruteforce():
-    """Pure-Python triple loop on tiny inputs (no numpy matmul), bias included."""
-    rng = np.random.default_rng(5)
-    x = rng.standard_normal((3, 7)).astype(np.float32)
-    w = rng.standard_normal((4, 7)).astype(np.float32)
-    b = rng.standard_normal(4).astype(np.float32)
-    got = oracle.router_logits(x, w, b)
-    for t in range(3):
-        for e in range(4):
-            acc = float(b[e])
-            for h in range(7):
-                acc += float(x[t, h]) * float(w[e, h])
-            assert abs(got[t, e] - acc) <= 1e-12 * (1 + abs(acc))
+    pins.check_router_bruteforce(oracle.router_logits)
 
 
 def test_router_logits_one_hot_rows():
-    """x = unit vectors: the logits are the router weight's columns (plus the bias), exactly."""
-    rng = np.random.default_rng(6)
-    w = rng.standard_normal((5, 8)).astype(np.float32)
-    b = rng.standard_normal(5).astype(np.float32)
-    got = oracle.router_logits(np.eye(8, dtype=np.float32), w, b)
-    assert np.array_equal(got, w.T.astype(np.float64) + b.astype(np.float64)[None, :])
-    assert np.array_equal(oracle.router_logits(np.eye(8, dtype=np.float32), w), w.T.astype(np.float64))
+    pins.check_router_one_hot(oracle.router_logits)
 
 
 @pytest.mark.parametrize("name", ["tiny", "prefill16k_zipf"])
@@ -240,72 +223,20 @@ def test_router_logits_reproduce_the_workload_logits(name):
 
 # ---------------------------------------------------------------------------- QK-Norm + half RoPE
 def test_head_rms_norm_closed_forms():
-    # a constant head c: every entry becomes sign(c) / sqrt(1 + eps / c^2) * w
-    w = np.linspace(0.5, 1.5, 8)
-    got = oracle.head_rms_norm(np.full((1, 8), -3.0), w, 1e-6)
-    assert np.allclose(got, -w / np.sqrt(1 + 1e-6 / 9.0), rtol=0, atol=1e-15)
-    # unit weight, eps 0: the result has mean square exactly 1 (up to rounding)
-    x = np.random.default_rng(1).standard_normal((5, 3, 16))
-    y = oracle.head_rms_norm(x, np.ones(16), 0.0)
-    assert np.allclose(np.mean(y * y, axis=-1), 1.0, atol=1e-14)
-    # scale invariance with eps = 0
-    assert np.allclose(oracle.head_rms_norm(7.5 * x, np.ones(16), 0.0), y, atol=1e-14)
+    pins.check_head_rms_norm(oracle.head_rms_norm)
+
+
+def test_rope_angles_hand_values():
+    pins.check_rope_angles(oracle.rope_angles)
 
 
 def test_rope_half_properties():
-    rng = np.random.default_rng(2)
-    x = rng.standard_normal((4, 2, 16))
-    rd = 8
-    # position 0 is the identity
-    a0 = oracle.rope_angles(np.zeros(4), rd, 10000.0)
-    assert np.array_equal(oracle.rope_half(x, a0, rd), x)
-    pos = np.array([1, 5, 17, 1000])
-    a = oracle.rope_angles(pos, rd, 10000.0)
-    y = oracle.rope_half(x, a, rd)
-    # the unrotated half passes through; each rotated pair keeps its length
-    assert np.array_equal(y[..., rd:], x[..., rd:])
-    h = rd // 2
-    assert np.allclose(y[..., :h] ** 2 + y[..., h:rd] ** 2, x[..., :h] ** 2 + x[..., h:rd] ** 2, atol=1e-12)
-    # rotations compose: rotate by p then by q == rotate by p + q
-    b = oracle.rope_angles(np.array([3, 4, 5, 6]), rd, 10000.0)
-    ab = oracle.rope_angles(pos + np.array([3, 4, 5, 6]), rd, 10000.0)
-    assert np.allclose(oracle.rope_half(y, b, rd), oracle.rope_half(x, ab, rd), atol=1e-10)
-    # pair 0 at position p is the complex product (x1 + i x2) * e^{i p} (theta^0 = 1)
-    z = (x[:, :, 0] + 1j * x[:, :, h]) * np.exp(1j * pos.astype(np.float64))[:, None]
-    assert np.allclose(y[:, :, 0], z.real, atol=1e-12) and np.allclose(y[:, :, h], z.imag, atol=1e-12)
+    pins.check_rope_half(oracle.rope_half, oracle.rope_angles)
 
 
 def test_qk_norm_rope_layout():
-    """q and k heads are normalised with their own weights and rotated; v passes through."""
-    rng = np.random.default_rng(3)
-    T, Hq, Hkv, D, rd = 3, 2, 1, 8, 4
-    qkv = rng.standard_normal((T, (Hq + 2 * Hkv) * D))
-    qw, kw = rng.uniform(0.5, 1.5, D), rng.uniform(0.5, 1.5, D)
-    pos = np.array([0, 2, 9])
-    out = oracle.qk_norm_rope(qkv, Hq, Hkv, D, rd, qw, kw, 1e-6, pos, 10000.0)
-    heads_in = qkv.reshape(T, Hq + 2 * Hkv, D)
-    heads = out.reshape(T, Hq + 2 * Hkv, D)
-    assert np.array_equal(heads[:, Hq + Hkv:], heads_in[:, Hq + Hkv:])            # v
-    assert np.allclose(heads[0, :Hq], oracle.head_rms_norm(heads_in[0, :Hq], qw, 1e-6))   # position 0: norm only
-    assert np.allclose(heads[0, Hq], oracle.head_rms_norm(heads_in[0, Hq], kw, 1e-6))
-    # dims past rotary_dim are the normalised values at every position
-    assert np.allclose(heads[:, :Hq, rd:], oracle.head_rms_norm(heads_in[:, :Hq], qw, 1e-6)[..., rd:])
+    pins.check_qk_layout(oracle.qk_norm_rope, oracle.head_rms_norm)
 
 
 def test_rope_interleaved_is_a_permuted_rope_half():
-    """Interleaved pairs (2i, 2i+1) become rotate-half pairs (i, i + rd/2) when the even
-    dims are moved to the front: the two arrangements differ only by that permutation."""
-    rng = np.random.default_rng(4)
-    D, rd = 16, 8
-    x = rng.standard_normal((3, 2, D))
-    ang = oracle.rope_angles(np.array([0, 7, 123]), rd, 500.0)
-    perm = np.concatenate([np.arange(0, rd, 2), np.arange(1, rd, 2), np.arange(rd, D)])
-    inv = np.argsort(perm)
-    via_half = oracle.rope_half(x[..., perm], ang, rd)[..., inv]
-    assert np.allclose(oracle.rope_interleaved(x, ang, rd), via_half, atol=1e-13)
-    # position 0 leaves x as it is; pair 0 at position p is (x0 + i x1) e^{i p}
-    assert np.array_equal(oracle.rope_interleaved(x[:1], ang[:1], rd), x[:1])
-    y = oracle.rope_interleaved(x, ang, rd)
-    z = (x[:, :, 0] + 1j * x[:, :, 1]) * np.exp(1j * np.array([0.0, 7.0, 123.0]))[:, None]
-    assert np.allclose(y[:, :, 0], z.real, atol=1e-12) and np.allclose(y[:, :, 1], z.imag, atol=1e-12)
-    assert np.array_equal(y[..., rd:], x[..., rd:])
+    pins.check_rope_interleaved(oracle.rope_interleaved, oracle.rope_half, oracle.rope_angles)
