@@ -40,6 +40,10 @@ def _outputs(layer):
     # blocks, many blocks per expert) and just past it (4104: the separate align runs)
     (small_cfg("fold_align_max", T=455, H=256, I=64, E=40, K=8, seed=27), 16),
     (small_cfg("fold_align_over", T=456, H=256, I=64, E=40, K=8, seed=28), 16),
+    # degenerate routing: the shared expert alone, and one routed expert
+    (small_cfg("shared_only", T=37, H=256, I=64, E=6, K=0, seed=31), 16),
+    (small_cfg("shared_only_wide", T=37, H=256, I=96, E=6, K=0, seed=31), 64),
+    (small_cfg("one_routed", T=29, H=256, I=64, E=1, K=1, seed=32), 16),
 ])
 def test_layer_forward_matches_four_calls(cfg, bm):
     inp = generate(cfg)
