@@ -107,6 +107,8 @@ SHAPES = [
     (9, 4, 0, 128, 32, True),      # q heads only
     (9, 0, 3, 128, 128, False),    # k (and v) heads only
     (1000, 12, 1, 128, 64, True),
+    (64, 96, 8, 128, 64, True),    # the unsharded attention (all 96 q and 8 kv heads on one GPU)
+    (3, 500, 262, 64, 32, True),   # 1024 heads per token, the limit
 ]
 
 
