@@ -93,7 +93,9 @@ int moe_router_logits(const uint16_t* x, const float* w_router, const float* bia
 size_t moe_router_workspace_bytes(int T, int H, int E); /* host */
 
 /* ---------------------------------------------------------------------------
- * The router gate folded into the route call: routing straight from x.
+ * The router gate folded into the route call: routing straight from x (the router
+ * scores every token over the routed experts ahead of the top-K: Optimizing GLM4-MoE
+ * for production, section 1; the fused routing table: intelliparadigm section 2.1).
  * moe_route_from_x = the gate of moe_router_logits followed by the routing of
  * moe_route_topk_plus_shared, with the gate's K-split partial tiles summed inside the
  * routing kernel (in chunk order, then + bias: the same float32 operations as the gate's
