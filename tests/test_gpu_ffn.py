@@ -199,7 +199,7 @@ def _sample_tokens(inp, n, seed):
     return np.array(sorted(pick))
 
 
-@pytest.mark.parametrize("name,bm,n", [("decode", 16, None), ("prefill", 64, 24),
+@pytest.mark.parametrize("name,bm,n", [("decode", 16, None), ("prefill", 64, 24), ("prefill", 128, 24),
                                        ("prefill16k_zipf", 128, 24), ("unsharded_block", 64, 8)])
 def test_ffn_full_size(name, bm, n):
     note(f"full {name}: generating inputs")

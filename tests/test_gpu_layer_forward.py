@@ -32,6 +32,7 @@ def _outputs(layer):
     (small_cfg("single_wg_align", T=455, H=256, I=64, E=40, K=8, seed=22), 64),  # 4095 entries: one-workgroup align
     (small_cfg("three_pass_align", T=600, H=256, I=64, E=40, K=8, seed=23), 64),  # 5400 entries: count/scan/scatter
     (CONFIGS["decode"], 16),
+    (CONFIGS["prefill"], 128),   # the bench's prefill launch configuration
     # decode-shaped blocks: routed experts with more than 16 entries (several row
     # blocks per expert), and I = 256
     (small_cfg("decode_multigroup", T=64, H=256, I=128, E=4, K=2, seed=24), 16),
