@@ -241,7 +241,13 @@ int moe_combine(int T, int K1, int H, const void* workspace, size_t ws_bytes, ui
  * above (K routed slots, E routed experts; K1 = K+1, E1 = E+1) and the same
  * outputs, bit for bit. The routing and the FP8 quantisation of x do not depend
  * on each other and share one launch, so the layer takes one launch fewer than
- * the four calls. align_ws/ffn_ws as for moe_align_by_expert/moe_fused_ffn.
+ * the four calls. With block_m == 128 and I <= 256 the shared expert's down GEMM
+ * and step 4 are one launch as well: the shared expert's rows (the last segment of
+ * the sorted layout, one per token) add the token's routed slot rows and store out,
+ * with the same float32 sum in the same order as moe_combine. align_ws/ffn_ws as for
+ * moe_align_by_expert/moe_fused_ffn; what ffn_ws holds afterwards is not part of the
+ * result (in that case the routed slot rows are kept in 128-column blocks and the
+ * shared expert's are not written).
  * ------------------------------------------------------------------------- */
 int moe_layer_forward(const uint16_t* x, const float* logits, const uint8_t* w13, const float* s13,
                       const uint8_t* w2, const float* s2, int scale_mode, int T, int H, int I, int E,

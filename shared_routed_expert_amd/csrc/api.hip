@@ -27,6 +27,10 @@ hipError_t launch_down(const uint8_t*, const float*, const uint8_t*, const float
                        const int32_t*, const int32_t*, const int32_t*, const float*, uint16_t*, int,
                        int, int, int, int, int, hipStream_t);
 hipError_t launch_combine(const uint16_t*, const uint16_t*, int, int, int, uint16_t*, hipStream_t);
+bool down_wide_supported(int I);
+hipError_t launch_down_wide_combine(const uint8_t*, const float*, const uint8_t*, const float*, bool,
+                                    const int32_t*, const int32_t*, const int32_t*, const float*, uint16_t*,
+                                    uint16_t*, int, int, int, int, int, hipStream_t);
 hipError_t launch_gate_up_decode(const uint8_t*, const float*, const uint8_t*, const float*, bool,
                                  const int32_t*, const int32_t*, float*, int, int, int, int, int,
                                  hipStream_t);
@@ -396,6 +400,23 @@ static int layer_forward(const uint16_t* x, const LogitSrc& src, const void* log
   st = moe_align_by_expert(topk_ids, T, K1, E1, block_m, sorted_slot_ids, block_expert, expert_counts,
                            expert_offsets, num_padded, align_ws, align_ws_bytes, stream);
   if (st != SRMOE_OK) return st;
+  if (block_m == 128 && down_wide_supported(I)) {
+    // prefill shapes: the shared expert's down GEMM and the combine are one launch (the
+    // shared expert's segment is the last one; its rows add the token's routed slot rows,
+    // left by the routed experts' down launch before it, and store out)
+    st = moe_ffn_gate_up(w13, s13, scale_mode, T, H, I, E1, K1, block_m, sorted_slot_ids, block_expert,
+                         num_padded, ffn_ws, ffn_ws_bytes, stream);
+    if (st != SRMOE_OK) return st;
+    const int P_max = (int)sorted_capacity(T, K1, E1, block_m);
+    st = hip_status(launch_quant_a(reinterpret_cast<const float*>(ws + L.a), P_max, I, blk, sorted_slot_ids,
+                                   topk_w, T * K1, reinterpret_cast<uint8_t*>(ws + L.aq),
+                                   reinterpret_cast<float*>(ws + L.sa), reinterpret_cast<float*>(ws + L.rs), sm));
+    if (st != SRMOE_OK) return st;
+    return hip_status(launch_down_wide_combine(
+        reinterpret_cast<const uint8_t*>(ws + L.aq), reinterpret_cast<const float*>(ws + L.sa), w2, s2, blk,
+        sorted_slot_ids, block_expert, expert_offsets + E, reinterpret_cast<const float*>(ws + L.rs),
+        reinterpret_cast<uint16_t*>(ws + L.slot_out), out, T, H, I, E1, K1, sm));
+  }
   st = moe_ffn_experts(w13, s13, w2, s2, scale_mode, T, H, I, E1, K1, block_m, sorted_slot_ids,
                        block_expert, num_padded, topk_w, ffn_ws, ffn_ws_bytes, stream);
   if (st != SRMOE_OK) return st;

@@ -396,34 +396,61 @@ __global__ void __launch_bounds__(256, 2) down_tile_kernel(
 // halves x 2 interleaved column streams over 128 * kDownTiles columns; tiles
 // are ordered row block major and walked per XCD.
 constexpr int kDownTiles = 4;
+constexpr int kCombTiles = 1;              // 64-column tiles per wavefront in the combining launch
 constexpr int kDownLD = 2 * kGroup + 16;   // LDS row stride of the a_q tile (bytes)
 constexpr int kStageLD = 128 + 16;         // LDS row stride of an output staging buffer
 
 typedef unsigned int u32x4_nt __attribute__((ext_vector_type(4)));
 
-template <bool kBlock, int KS>
+// acc[c] += the c-th of the 8 bf16 values in v (low half of each word first)
+__device__ __forceinline__ void add_bf16x8(float (&acc)[8], const uint4& v) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    acc[2 * j] += bf16_to_f32(w[j] & 0xFFFFu);
+    acc[2 * j + 1] += bf16_to_f32(w[j] >> 16);
+  }
+}
+
+// Where the rows' bf16 results go (kOut):
+//  kRowsOut    the blocks of rows 0 .. rows[0] - 1; each row's result to its slot row of
+//              slot_out, [T*K1 + 1, H] (moe_ffn_down's layout);
+//  kBlockedOut the same rows, with slot_out in 128-column blocks: the piece of slot row
+//              s at columns 128 cb .. 128 cb + 127 at element (cb * (T*K1 + 1) + s) * 128;
+//  kCombineOut the comb_blocks blocks from row rows[0] on (the shared expert's segment,
+//              one row per token in token order); each row's result is added to the
+//              token's routed slot rows, left column-blocked in slot_out by a kBlockedOut
+//              launch over the rows before, and the sum is stored to out.
+// In the blocked layout the combining launch reads, per 128-token block and column block,
+// one contiguous run of 128 * K1 pieces of 256 bytes (the row layout scatters them).
+constexpr int kRowsOut = 0, kBlockedOut = 1, kCombineOut = 2;
+template <bool kBlock, int KS, int NTL, int kOut>
 __global__ void __launch_bounds__(256, 2) down_wide_kernel(
     const uint8_t* __restrict__ aq, const float* __restrict__ sa, const uint8_t* __restrict__ w2,
     const float* __restrict__ s2, const int32_t* __restrict__ sorted,
-    const int32_t* __restrict__ block_expert, const int32_t* __restrict__ num_padded,
+    const int32_t* __restrict__ block_expert, const int32_t* __restrict__ rows,
     const float* __restrict__ row_scale, uint16_t* __restrict__ slot_out, int T, int H, int I,
-    int K1) {
-  constexpr int kCols = 128 * kDownTiles;   // columns per workgroup
+    int K1, uint16_t* __restrict__ out, int comb_blocks) {
+  constexpr int kCols = 128 * NTL;   // columns per workgroup
   __shared__ __align__(16) uint8_t atile[kTBM * kDownLD];
   __shared__ __align__(16) uint8_t stage[4][64 * kStageLD];
   __shared__ __align__(16) float scol[kBlock ? kCols / kGroup * KS : kCols];
   const int ng = (H + kCols - 1) / kCols;
-  const int tile = xcd_tile(blockIdx.x, num_padded[0] / kTBM * ng);
+  constexpr bool kComb = kOut == kCombineOut;
+  const int tile = xcd_tile(blockIdx.x, (kComb ? comb_blocks : rows[0] / kTBM) * ng);
   if (tile < 0) return;
-  const int b = tile / ng;
+  const int bt = tile / ng;
+  const int b = kComb ? rows[0] / kTBM + bt : bt;
   const int e = block_expert[b];
   if (e < 0) return;
-  const int g = tile - b * ng;
+  const int g = tile - bt * ng;
   const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
   const int r16 = lane & 15, kq = lane >> 4;
   const int wt = wv & 1, wc = wv >> 1;
   const int nct = H / 64;
   const int sentinel = T * K1;
+  const uint64_t magic = slot_div_magic(K1);
+  const size_t nrows = (size_t)sentinel + 1;   // slot rows, with the padding rows' spare
   const int c0 = g * kCols;   // first column of the workgroup
 
   // a_q rows of the block -> LDS, bytes [I, KS * 128) of each row zeroed: 4 * KS
@@ -445,10 +472,7 @@ __global__ void __launch_bounds__(256, 2) down_wide_kernel(
   // block mode: per 128-column block and K step), clamped past H
   if (!kBlock) {
 #pragma unroll
-    for (int i = 0; i < kCols / 256; ++i) {
-      const int c = tid + 256 * i;
-      scol[c] = s2[(size_t)e * H + min(c0 + c, H - 1)];
-    }
+    for (int c = tid; c < kCols; c += 256) scol[c] = s2[(size_t)e * H + min(c0 + c, H - 1)];
   } else if (tid < kCols / kGroup * KS) {
     const int cb = min(c0 / kGroup + tid / KS, H / kGroup - 1);
     scol[tid] = s2[((size_t)e * (H / kGroup) + cb) * (I / kGroup) + tid % KS];
@@ -476,7 +500,7 @@ __global__ void __launch_bounds__(256, 2) down_wide_kernel(
     const int k = ks * kGroup + kq * 32;
     koff[ks] = k < I ? k : 0;
   }
-  int t = g * 2 * kDownTiles + wc;   // this wavefront's first 64-column tile
+  int t = g * 2 * NTL + wc;   // this wavefront's first 64-column tile
   const bool active = t < nct;
   const int t0 = active ? t : 0;
   // weight fragment rows: row r16 of MFMA tile n is column (r16/4)*16 + 4n + r16%4
@@ -492,7 +516,28 @@ __global__ void __launch_bounds__(256, 2) down_wide_kernel(
       for (int ks = 0; ks < KS; ++ks) w[n][ks] = load32(wb + (size_t)(tile * 64 + 4 * n) * I + koff[ks]);
   };
   wload(wf[0], t0);
-  wload(wf[1], min(t0 + 2, nct - 1));
+  if (NTL > 1) wload(wf[1], min(t0 + 2, nct - 1));
+  // combining launch (one 64-column tile per wavefront): the slot rows that the first two
+  // rows add do not depend on the GEMM, so their loads go out now
+  static_assert(!kComb || NTL == 1, "the combining launch takes one tile per wavefront");
+  const int nr = K1 - 1;
+  const int last = nr > 0 ? nr - 1 : 0;
+  const int hs0 = t0 * 64 + (lane & 7) * 8;
+  const size_t cbase = (size_t)(hs0 >> 7) * nrows;   // the column block's first row
+  const int hc = hs0 & 127;
+  uint4 sv[2][2][8];
+  auto slot_issue = [&](int q, uint4 (&v)[2][8]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int first = srow[q + u] < sentinel ? srow[q + u] - nr : 0;
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        v[u][k] = *reinterpret_cast<const uint4*>(slot_out + (cbase + first + min(k, last)) * 128 + hc);
+    }
+  };
+  // (not with block scales over two K steps: their extra live registers would spill)
+  constexpr bool kEarly = kComb && !(kBlock && KS == 2);
+  if (kEarly) slot_issue(0, sv[0]);
   __syncthreads();   // the a_q tile and the scales are in LDS
   if (!active) return;
 
@@ -500,7 +545,7 @@ __global__ void __launch_bounds__(256, 2) down_wide_kernel(
   const uint8_t* trow = &atile[(64 * wt + r16) * kDownLD + kq * 32];
   uint8_t* stg = stage[wv];
 #pragma unroll
-  for (int j = 0; j < kDownTiles; ++j) {
+  for (int j = 0; j < NTL; ++j) {
     const int cur = j & 1;
     const int tj = t + 2 * j;
     if (tj >= nct) break;
@@ -531,7 +576,7 @@ __global__ void __launch_bounds__(256, 2) down_wide_kernel(
         }
       __builtin_amdgcn_sched_barrier(0);
     }
-    if (j + 2 < kDownTiles) wload(wf[cur], tl);
+    if (j + 2 < NTL) wload(wf[cur], tl);
     __builtin_amdgcn_sched_barrier(0);
     // scale, round and stage: lane (r16, kq) holds columns 16 kq .. 16 kq + 15 of
     // rows 16 m + r16 of the wavefront's 64
@@ -558,11 +603,47 @@ __global__ void __launch_bounds__(256, 2) down_wide_kernel(
     // store: 8 lanes per row, 8 rows per instruction, each row's 128 bytes whole
     // (a wavefront's LDS operations complete in order, so no barrier is needed)
     const int hs = tj * 64 + (lane & 7) * 8;
+    if (!kComb) {
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const uint4 v = *reinterpret_cast<const uint4*>(stg + (8 * q + (lane >> 3)) * kStageLD + (lane & 7) * 16);
-      const u32x4_nt nv = {v.x, v.y, v.z, v.w};
-      __builtin_nontemporal_store(nv, reinterpret_cast<u32x4_nt*>(slot_out + (size_t)srow[q] * H + hs));
+      for (int q = 0; q < 8; ++q) {
+        const uint4 v = *reinterpret_cast<const uint4*>(stg + (8 * q + (lane >> 3)) * kStageLD + (lane & 7) * 16);
+        const u32x4_nt nv = {v.x, v.y, v.z, v.w};
+        const size_t o = kOut == kRowsOut ? (size_t)srow[q] * H + hs
+                                          : ((size_t)(hs >> 7) * nrows + srow[q]) * 128 + (hs & 127);
+        __builtin_nontemporal_store(nv, reinterpret_cast<u32x4_nt*>(slot_out + o));
+      }
+    } else {
+      // the combine's sum for the row's token t: float32 from 0, routed slot rows t*K1 ..
+      // t*K1 + K1 - 2 in order, then this row's bf16 value (slot K1 - 1). Two rows at a
+      // time with the next two rows' slot loads in flight; slots 0..7 are always loaded
+      // (a row past the token's last is masked to +0.0, which leaves a sum that started
+      // at +0.0 unchanged), slots 8.. one at a time. Padding rows read token 0's rows and
+      // store nothing.
+      if (!kEarly) slot_issue(0, sv[0]);
+#pragma unroll
+      for (int q = 0; q < 8; q += 2) {
+        if (q + 2 < 8) slot_issue(q + 2, sv[((q >> 1) + 1) & 1]);
+        uint4 (&v)[2][8] = sv[(q >> 1) & 1];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int srw = srow[q + u];
+          float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int k = 0; k < 8; ++k) {
+            const uint32_t m = k < nr ? 0xFFFFFFFFu : 0u;
+            add_bf16x8(acc, make_uint4(v[u][k].x & m, v[u][k].y & m, v[u][k].z & m, v[u][k].w & m));
+          }
+          const int first = srw < sentinel ? srw - nr : 0;
+          for (int k = 8; k < nr; ++k)
+            add_bf16x8(acc, *reinterpret_cast<const uint4*>(slot_out + (cbase + first + k) * 128 + hc));
+          add_bf16x8(acc, *reinterpret_cast<const uint4*>(stg + (8 * (q + u) + (lane >> 3)) * kStageLD + (lane & 7) * 16));
+          if (srw < sentinel) {
+            const u32x4_nt nv = {pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]),
+                                 pack_bf16x2(acc[4], acc[5]), pack_bf16x2(acc[6], acc[7])};
+            __builtin_nontemporal_store(nv, reinterpret_cast<u32x4_nt*>(out + (size_t)slot_token(srw, magic) * H + hs));
+          }
+        }
+      }
     }
   }
 }
@@ -575,9 +656,9 @@ hipError_t launch_down_tile(const uint8_t* aq, const float* sa, const uint8_t* w
   const dim3 blk(256);
   if (I <= 2 * kGroup) {
     const dim3 grid(nb * ((H + 128 * kDownTiles - 1) / (128 * kDownTiles)));
-#define SRMOE_DOWN_WIDE(B, KS)                                                                   \
-  hipLaunchKernelGGL((down_wide_kernel<B, KS>), grid, blk, 0, stream, aq, sa, w2, s2, sorted,  \
-                     block_expert, num_padded, row_scale, slot_out, T, H, I, K1)
+#define SRMOE_DOWN_WIDE(B, KS)                                                                        \
+  hipLaunchKernelGGL((down_wide_kernel<B, KS, kDownTiles, kRowsOut>), grid, blk, 0, stream, aq, sa, w2, s2, \
+                     sorted, block_expert, num_padded, row_scale, slot_out, T, H, I, K1, nullptr, 0)
     if (I <= kGroup) {
       if (block) SRMOE_DOWN_WIDE(true, 1); else SRMOE_DOWN_WIDE(false, 1);
     } else {
@@ -593,6 +674,42 @@ hipError_t launch_down_tile(const uint8_t* aq, const float* sa, const uint8_t* w
   else
     hipLaunchKernelGGL(down_tile_kernel<false>, grid, blk, 0, stream, aq, sa, w2, s2, sorted,
                        block_expert, num_padded, row_scale, slot_out, T, H, I, K1);
+  return hipGetLastError();
+}
+
+bool down_wide_supported(int I) { return I <= 2 * kGroup; }
+
+// The down GEMM and the combine of the layer in two launches: the routed experts' rows
+// (those before the shared expert's segment, which starts at row *shared_first) to
+// slot_out in the column-blocked layout, then the shared expert's ceil(T / 128) blocks,
+// whose rows add the token's routed slot rows and store out. The shared expert's slot
+// rows are never written.
+hipError_t launch_down_wide_combine(const uint8_t* aq, const float* sa, const uint8_t* w2, const float* s2,
+                                    bool block, const int32_t* sorted, const int32_t* block_expert,
+                                    const int32_t* shared_first, const float* row_scale,
+                                    uint16_t* slot_out, uint16_t* out, int T, int H, int I, int E1, int K1,
+                                    hipStream_t stream) {
+  if (!down_wide_supported(I)) return hipErrorInvalidValue;
+  const int nb = (int)(sorted_capacity(T, K1, E1, kTBM) / kTBM);
+  const int nbs = (T + kTBM - 1) / kTBM;
+  const dim3 blk(256);
+  const dim3 grid(nb * ((H + 128 * kDownTiles - 1) / (128 * kDownTiles)));
+  const dim3 grid_c(nbs * ((H + 128 * kCombTiles - 1) / (128 * kCombTiles)));
+#define SRMOE_DOWN_COMB(B, KS)                                                                          \
+  do {                                                                                                  \
+    hipLaunchKernelGGL((down_wide_kernel<B, KS, kDownTiles, kBlockedOut>), grid, blk, 0, stream, aq, sa, w2, \
+                       s2, sorted, block_expert, shared_first, row_scale, slot_out, T, H, I, K1, nullptr, \
+                       0);                                                                              \
+    hipLaunchKernelGGL((down_wide_kernel<B, KS, kCombTiles, kCombineOut>), grid_c, blk, 0, stream, aq, sa, w2, \
+                       s2, sorted, block_expert, shared_first, row_scale, slot_out, T, H, I, K1, out,  \
+                       nbs);                                                                            \
+  } while (0)
+  if (I <= kGroup) {
+    if (block) SRMOE_DOWN_COMB(true, 1); else SRMOE_DOWN_COMB(false, 1);
+  } else {
+    if (block) SRMOE_DOWN_COMB(true, 2); else SRMOE_DOWN_COMB(false, 2);
+  }
+#undef SRMOE_DOWN_COMB
   return hipGetLastError();
 }
 

@@ -45,6 +45,15 @@ def _outputs(layer):
     (small_cfg("shared_only", T=37, H=256, I=64, E=6, K=0, seed=31), 16),
     (small_cfg("shared_only_wide", T=37, H=256, I=96, E=6, K=0, seed=31), 64),
     (small_cfg("one_routed", T=29, H=256, I=64, E=1, K=1, seed=32), 16),
+    # 128-row blocks: the shared expert's down GEMM and the combine in one launch. Ragged
+    # last blocks, column groups past H, the shared expert alone (no routed slot to add),
+    # 15 routed slots (two rounds of slot loads), block scales with one and two K steps
+    (small_cfg("ragged", T=77, H=384, I=96, E=12, K=3, seed=11), 128),
+    (small_cfg("three_blocks", T=300, H=640, I=192, E=20, K=8, seed=33), 128),
+    (small_cfg("shared_only", T=37, H=256, I=64, E=6, K=0, seed=31), 128),
+    (small_cfg("edge_e255", T=30, H=256, I=64, E=255, K=15, seed=21), 128),
+    (small_cfg("block", T=50, H=384, I=256, E=6, K=2, mode="block128", seed=15), 128),
+    (small_cfg("block_i128", T=140, H=256, I=128, E=5, K=2, mode="block128", seed=34), 128),
 ])
 def test_layer_forward_matches_four_calls(cfg, bm):
     inp = generate(cfg)
