@@ -33,6 +33,7 @@ def _outputs(layer):
     (small_cfg("three_pass_align", T=600, H=256, I=64, E=40, K=8, seed=23), 64),  # 5400 entries: count/scan/scatter
     (CONFIGS["decode"], 16),
     (CONFIGS["prefill"], 128),   # the bench's prefill launch configuration
+    (CONFIGS["prefill16k_zipf"], 128),   # 16,384 tokens, one expert with 13,856 of them
     # decode-shaped blocks: routed experts with more than 16 entries (several row
     # blocks per expert), and I = 256
     (small_cfg("decode_multigroup", T=64, H=256, I=128, E=4, K=2, seed=24), 16),
