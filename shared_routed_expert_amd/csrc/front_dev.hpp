@@ -125,6 +125,23 @@ __device__ __forceinline__ float amax4(float4 v) {
   return fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
 }
 
+// 8 bf16 values, low half of each word first
+__device__ __forceinline__ float4 bf16x4_lo(const uint4& v) {
+  return make_float4(bf16_to_f32(v.x & 0xFFFFu), bf16_to_f32(v.x >> 16), bf16_to_f32(v.y & 0xFFFFu),
+                     bf16_to_f32(v.y >> 16));
+}
+__device__ __forceinline__ float4 bf16x4_hi(const uint4& v) {
+  return make_float4(bf16_to_f32(v.z & 0xFFFFu), bf16_to_f32(v.z >> 16), bf16_to_f32(v.w & 0xFFFFu),
+                     bf16_to_f32(v.w >> 16));
+}
+__device__ __forceinline__ float amax_bf16x8(const uint4& v) {
+  return fmaxf(amax4(bf16x4_lo(v)), amax4(bf16x4_hi(v)));
+}
+__device__ __forceinline__ uint2 encode_bf16x8(const uint4& v, const ScaleDiv& q) {
+  const float4 a = bf16x4_lo(v), b = bf16x4_hi(v);
+  return make_uint2(encode4(a.x, a.y, a.z, a.w, q), encode4(b.x, b.y, b.z, b.w, q));
+}
+
 // FP8 quantisation of token t's row of x by a group of 256 threads (tid 0..255);
 // red points at 4 LDS floats owned by the group. Per-channel: one scale for the row
 // (one pass while H <= 8192); block mode: one scale per 128 columns. Contains
@@ -138,17 +155,20 @@ __device__ __forceinline__ void quant_x_token(const uint16_t* __restrict__ x, in
   const uint16_t* row = x + (size_t)t * H;
   uint8_t* qrow = xq + (size_t)t * H;
   if (!kBlock) {
-    constexpr int kMaxStripes = 8;
-    float4 v[kMaxStripes];
+    // 8 values (16 bytes) per thread and stripe: up to 4 stripes of 2048 values stay in
+    // registers between the absmax and the encode (one pass while H <= 8192)
+    constexpr int kMaxStripes = 4;
+    uint4 v[kMaxStripes];
     float amax = 0.0f;
 #pragma unroll
     for (int i = 0; i < kMaxStripes; ++i) {
-      const int h = i * 1024 + tid * 4;
-      v[i] = (valid && h < H) ? load_bf16x4(row + h) : make_float4(0.f, 0.f, 0.f, 0.f);
-      amax = fmaxf(amax, amax4(v[i]));
+      const int h = i * 2048 + tid * 8;
+      v[i] = (valid && h < H) ? *reinterpret_cast<const uint4*>(row + h) : make_uint4(0u, 0u, 0u, 0u);
+      amax = fmaxf(amax, amax_bf16x8(v[i]));
     }
     if (valid)
-      for (int h = kMaxStripes * 1024 + tid * 4; h < H; h += 1024) amax = fmaxf(amax, amax4(load_bf16x4(row + h)));
+      for (int h = kMaxStripes * 2048 + tid * 8; h < H; h += 2048)
+        amax = fmaxf(amax, amax_bf16x8(*reinterpret_cast<const uint4*>(row + h)));
     amax = wave_max(amax);
     if (lane == 0) red[wv] = amax;
     __syncthreads();
@@ -158,13 +178,11 @@ __device__ __forceinline__ void quant_x_token(const uint16_t* __restrict__ x, in
     const ScaleDiv q = scale_div(scale);
 #pragma unroll
     for (int i = 0; i < kMaxStripes; ++i) {
-      const int h = i * 1024 + tid * 4;
-      if (h < H) *reinterpret_cast<uint32_t*>(qrow + h) = encode4(v[i].x, v[i].y, v[i].z, v[i].w, q);
+      const int h = i * 2048 + tid * 8;
+      if (h < H) *reinterpret_cast<uint2*>(qrow + h) = encode_bf16x8(v[i], q);
     }
-    for (int h = kMaxStripes * 1024 + tid * 4; h < H; h += 1024) {
-      const float4 u = load_bf16x4(row + h);
-      *reinterpret_cast<uint32_t*>(qrow + h) = encode4(u.x, u.y, u.z, u.w, q);
-    }
+    for (int h = kMaxStripes * 2048 + tid * 8; h < H; h += 2048)
+      *reinterpret_cast<uint2*>(qrow + h) = encode_bf16x8(*reinterpret_cast<const uint4*>(row + h), q);
   } else {
     if (!valid) return;
     // 128-wide groups are 32 consecutive threads; H % 128 == 0 keeps every group whole.
