@@ -18,8 +18,8 @@ size_t align_workspace_bytes(int T, int K1, int E1);
 hipError_t launch_align(const int32_t*, int, int, int, int, int32_t*, int32_t*, int32_t*, int32_t*,
                         int32_t*, void*, hipStream_t);
 hipError_t launch_quant_x(const uint16_t*, int, int, bool, uint8_t*, float*, hipStream_t);
-hipError_t launch_quant_a(const float*, int, int, bool, const int32_t*, const float*, int, uint8_t*,
-                          float*, float*, hipStream_t);
+hipError_t launch_quant_a(const float*, int, int, bool, const int32_t*, const float*, int, const int32_t*,
+                          uint8_t*, float*, float*, hipStream_t);
 hipError_t launch_gate_up(const uint8_t*, const float*, const uint8_t*, const float*, bool,
                           const int32_t*, const int32_t*, const int32_t*, float*, int, int, int, int,
                           int, int, hipStream_t);
@@ -279,7 +279,7 @@ int moe_ffn_down(const uint8_t* w2, const float* s2, int scale_mode, int T, int 
   const bool blk = scale_mode == SRMOE_SCALE_BLOCK128;
   const int P_max = (int)sorted_capacity(T, K1, E1, block_m);
   hipError_t e = launch_quant_a(reinterpret_cast<const float*>(ws + L.a), P_max, I, blk,
-                                sorted_slot_ids, topk_w, T * K1,
+                                sorted_slot_ids, topk_w, T * K1, num_padded,
                                 reinterpret_cast<uint8_t*>(ws + L.aq),
                                 reinterpret_cast<float*>(ws + L.sa),
                                 reinterpret_cast<float*>(ws + L.rs), as_stream(stream));
@@ -409,7 +409,7 @@ static int layer_forward(const uint16_t* x, const LogitSrc& src, const void* log
     if (st != SRMOE_OK) return st;
     const int P_max = (int)sorted_capacity(T, K1, E1, block_m);
     st = hip_status(launch_quant_a(reinterpret_cast<const float*>(ws + L.a), P_max, I, blk, sorted_slot_ids,
-                                   topk_w, T * K1, reinterpret_cast<uint8_t*>(ws + L.aq),
+                                   topk_w, T * K1, num_padded, reinterpret_cast<uint8_t*>(ws + L.aq),
                                    reinterpret_cast<float*>(ws + L.sa), reinterpret_cast<float*>(ws + L.rs), sm));
     if (st != SRMOE_OK) return st;
     return hip_status(launch_down_wide_combine(

@@ -26,11 +26,11 @@ template <bool kBlock>
 __global__ void __launch_bounds__(256) quant_a_kernel(const float* __restrict__ a, int I,
                                                       const int32_t* __restrict__ sorted,
                                                       const float* __restrict__ topk_w, int sentinel,
+                                                      const int32_t* __restrict__ num_padded,
                                                       uint8_t* __restrict__ aq, float* __restrict__ sa,
                                                       float* __restrict__ row_scale) {
-  // Every row up to the sort capacity is processed: rows past the used blocks hold
-  // stale data whose codes no GEMM reads, and skipping the block check saves a
-  // dependent load at the start.
+  // Rows past the used blocks (a multiple of 16 rows) are skipped: no GEMM reads them.
+  if ((int)blockIdx.x * 16 >= num_padded[0]) return;
   const int p = blockIdx.x * 16 + (threadIdx.x >> 4);
   const int part = threadIdx.x & 15;
   const float* row = a + (size_t)p * I;
@@ -41,19 +41,19 @@ __global__ void __launch_bounds__(256) quant_a_kernel(const float* __restrict__ 
     if (s < sentinel) wgt = topk_w[s];
   }
   if (!kBlock) {
-    // one pass for I <= 512 (16 stripes of 2 values per thread), else two
-    constexpr int kMaxStripes = 16;
-    float2 v[kMaxStripes];
+    // one pass for I <= 512 (8 stripes of 4 values per thread), else two
+    constexpr int kMaxStripes = 8;
+    float4 v[kMaxStripes];
     float amax = 0.0f;
 #pragma unroll
     for (int j = 0; j < kMaxStripes; ++j) {
-      const int i = j * 32 + part * 2;
-      v[j] = i < I ? *reinterpret_cast<const float2*>(row + i) : make_float2(0.f, 0.f);
-      amax = fmaxf(amax, fmaxf(fabsf(v[j].x), fabsf(v[j].y)));
+      const int i = j * 64 + part * 4;
+      v[j] = i < I ? *reinterpret_cast<const float4*>(row + i) : make_float4(0.f, 0.f, 0.f, 0.f);
+      amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v[j].x), fabsf(v[j].y)), fmaxf(fabsf(v[j].z), fabsf(v[j].w))));
     }
-    for (int i = kMaxStripes * 32 + part * 2; i < I; i += 32) {
-      const float2 w = *reinterpret_cast<const float2*>(row + i);
-      amax = fmaxf(amax, fmaxf(fabsf(w.x), fabsf(w.y)));
+    for (int i = kMaxStripes * 64 + part * 4; i < I; i += 64) {
+      const float4 w = *reinterpret_cast<const float4*>(row + i);
+      amax = fmaxf(amax, fmaxf(fmaxf(fabsf(w.x), fabsf(w.y)), fmaxf(fabsf(w.z), fabsf(w.w))));
     }
     const float scale = fp8_scale(row16_max(amax));
     if (part == 0) {
@@ -63,13 +63,13 @@ __global__ void __launch_bounds__(256) quant_a_kernel(const float* __restrict__ 
     const ScaleDiv q = scale_div(scale);
 #pragma unroll
     for (int j = 0; j < kMaxStripes; ++j) {
-      const int i = j * 32 + part * 2;
+      const int i = j * 64 + part * 4;
       if (i < I)
-        *reinterpret_cast<uint16_t*>(qrow + i) = (uint16_t)quant2(q, v[j].x, v[j].y);
+        *reinterpret_cast<uint32_t*>(qrow + i) = quant2(q, v[j].x, v[j].y) | (quant2(q, v[j].z, v[j].w) << 16);
     }
-    for (int i = kMaxStripes * 32 + part * 2; i < I; i += 32) {
-      const float2 w = *reinterpret_cast<const float2*>(row + i);
-      *reinterpret_cast<uint16_t*>(qrow + i) = (uint16_t)quant2(q, w.x, w.y);
+    for (int i = kMaxStripes * 64 + part * 4; i < I; i += 64) {
+      const float4 w = *reinterpret_cast<const float4*>(row + i);
+      *reinterpret_cast<uint32_t*>(qrow + i) = quant2(q, w.x, w.y) | (quant2(q, w.z, w.w) << 16);
     }
   } else {
     if (part == 0) row_scale[p] = wgt;
@@ -102,13 +102,13 @@ hipError_t launch_quant_x(const uint16_t* x, int T, int H, bool block, uint8_t* 
 }
 
 hipError_t launch_quant_a(const float* a, int P_max, int I, bool block, const int32_t* sorted,
-                          const float* topk_w, int sentinel, uint8_t* aq, float* sa, float* row_scale,
-                          hipStream_t stream) {
+                          const float* topk_w, int sentinel, const int32_t* num_padded, uint8_t* aq,
+                          float* sa, float* row_scale, hipStream_t stream) {
   const dim3 grid(P_max / 16), blk(256);
   if (block)
-    hipLaunchKernelGGL(quant_a_kernel<true>, grid, blk, 0, stream, a, I, sorted, topk_w, sentinel, aq, sa, row_scale);
+    hipLaunchKernelGGL(quant_a_kernel<true>, grid, blk, 0, stream, a, I, sorted, topk_w, sentinel, num_padded, aq, sa, row_scale);
   else
-    hipLaunchKernelGGL(quant_a_kernel<false>, grid, blk, 0, stream, a, I, sorted, topk_w, sentinel, aq, sa, row_scale);
+    hipLaunchKernelGGL(quant_a_kernel<false>, grid, blk, 0, stream, a, I, sorted, topk_w, sentinel, num_padded, aq, sa, row_scale);
   return hipGetLastError();
 }
 
