@@ -55,6 +55,9 @@ def _outputs(layer):
     (small_cfg("edge_e255", T=30, H=256, I=64, E=255, K=15, seed=21), 128),
     (small_cfg("block", T=50, H=384, I=256, E=6, K=2, mode="block128", seed=15), 128),
     (small_cfg("block_i128", T=140, H=256, I=128, E=5, K=2, mode="block128", seed=34), 128),
+    # the smallest shapes: one token; H = 128 (one column group), I = 32 (a partial K step)
+    (small_cfg("one_token", T=1, H=256, I=64, E=20, K=8, seed=35), 128),
+    (small_cfg("h128_i32", T=200, H=128, I=32, E=8, K=2, seed=36), 128),
 ])
 def test_layer_forward_matches_four_calls(cfg, bm):
     inp = generate(cfg)
