@@ -58,6 +58,9 @@ def _outputs(layer):
     # the smallest shapes: one token; H = 128 (one column group), I = 32 (a partial K step)
     (small_cfg("one_token", T=1, H=256, I=64, E=20, K=8, seed=35), 128),
     (small_cfg("h128_i32", T=200, H=128, I=32, E=8, K=2, seed=36), 128),
+    # I > 256 at block_m 128: the K-looped down GEMM and the separate combine
+    (small_cfg("wide_i384_block", T=150, H=256, I=384, E=6, K=2, mode="block128", seed=37), 128),
+    (small_cfg("wide_i320", T=90, H=384, I=320, E=7, K=3, seed=38), 128),
 ])
 def test_layer_forward_matches_four_calls(cfg, bm):
     inp = generate(cfg)
