@@ -227,3 +227,35 @@ def test_ffn_full_size(name, bm, n):
     full = layer.out.float()
     assert torch.isfinite(full).all()
     assert (full.abs().amax(dim=1) > 0).all()
+
+
+@pytest.mark.parametrize("name,bm,n", [("decode", 16, None), ("prefill", 128, 24), ("prefill16k_zipf", 128, 16)])
+def test_layer_forward_full_size_against_oracle(name, bm, n):
+    """moe_layer_forward itself, in the launch configuration bench.py times, against the
+    oracle: every token at decode, sampled tokens (the hottest expert's first and last
+    among them) at the prefill sizes; the routing and sorted layout exactly."""
+    note(f"layer full {name}: generating inputs")
+    inp = generate(CONFIGS[name])
+    c = inp.cfg
+    layer, W = make_layer(inp, bm)
+    note(f"layer full {name}: moe_layer_forward bm={bm}")
+    layer.forward_fused(bf16_dev(inp.x_bf16), to_dev(inp.logits), W, 1.0)
+    torch.cuda.synchronize()
+    ids_ref, w_ref = oracle.route_topk_plus_shared(inp.logits, c.K)
+    assert np.array_equal(layer.topk_ids.cpu().numpy(), ids_ref)
+    s, b, cnt, off, npad = oracle.align_by_expert(ids_ref, c.E1, bm)
+    assert np.array_equal(layer.sorted_slot_ids.cpu().numpy(), s)
+    assert np.array_equal(layer.block_expert.cpu().numpy(), b)
+    assert np.array_equal(layer.expert_counts.cpu().numpy(), cnt)
+    assert np.array_equal(layer.expert_offsets.cpu().numpy(), off)
+    tokens = None if n is None else _sample_tokens(inp, n, seed=c.seed + 1)
+    note(f"layer full {name}: oracle on {c.T if tokens is None else len(tokens)} tokens")
+    out_ref = oracle.moe_fused(x_f32(inp), inp.logits, c.K, inp.w13_q, inp.s13, inp.w2_q, inp.s2, tokens=tokens)
+    tok = np.arange(c.T) if tokens is None else tokens
+    out = bf16_to_np(layer.out)[tok]
+    e, n_tie = check_rows_with_ties(out, out_ref, inp, [[(int(t), k) for k in range(c.K1)] for t in tok],
+                                    ids_ref, w_ref)
+    note(f"layer full {name}: max per-token rel err {e:.3e}, tokens on the tie allowance: {n_tie}")
+    full = layer.out.float()
+    assert torch.isfinite(full).all()
+    assert (full.abs().amax(dim=1) > 0).all()
