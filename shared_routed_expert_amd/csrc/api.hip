@@ -46,7 +46,7 @@ struct AlignOut {
   int E1;
 };
 hipError_t launch_expert_ffn_decode(const uint8_t*, const float*, const uint8_t*, const float*,
-                                    const uint8_t*, const float*, bool, int32_t*, int32_t*,
+                                    const uint8_t*, const float*, bool, int32_t*, int32_t*, const int32_t*,
                                     const AlignOut*, const float*, float*, uint16_t*, int, int, int,
                                     int, int, hipStream_t);
 hipError_t launch_qk_norm_rope(uint16_t*, int, int, int, int, int, bool, const float*, const float*, float,
@@ -325,7 +325,7 @@ int moe_ffn_experts(const uint8_t* w13, const float* s13, const uint8_t* w2, con
   return hip_status(launch_expert_ffn_decode(
       reinterpret_cast<const uint8_t*>(ws + L.xq), reinterpret_cast<const float*>(ws + L.sx), w13, s13,
       w2, s2, scale_mode == SRMOE_SCALE_BLOCK128, const_cast<int32_t*>(sorted_slot_ids),
-      const_cast<int32_t*>(block_expert), nullptr, topk_w, reinterpret_cast<float*>(ws + L.a),
+      const_cast<int32_t*>(block_expert), num_padded, nullptr, topk_w, reinterpret_cast<float*>(ws + L.a),
       reinterpret_cast<uint16_t*>(ws + L.slot_out), T, H, I, E1, K1, as_stream(stream)));
 }
 
@@ -391,7 +391,7 @@ static int layer_forward(const uint16_t* x, const LogitSrc& src, const void* log
     const AlignOut al{topk_ids, expert_counts, expert_offsets, num_padded, E1};
     st = hip_status(launch_expert_ffn_decode(
         reinterpret_cast<const uint8_t*>(ws + L.xq), reinterpret_cast<const float*>(ws + L.sx), w13,
-        s13, w2, s2, blk, sorted_slot_ids, block_expert, &al, topk_w,
+        s13, w2, s2, blk, sorted_slot_ids, block_expert, num_padded, &al, topk_w,
         reinterpret_cast<float*>(ws + L.a), reinterpret_cast<uint16_t*>(ws + L.slot_out), T, H, I,
         E1, K1, sm));
     if (st != SRMOE_OK) return st;

@@ -107,6 +107,7 @@ __global__ void __launch_bounds__(512) expert_ffn_decode_kernel(
   __shared__ float s13s[kBlock ? (2 * I / kGroup) * kXMaxHB : 1];   // w13[e]'s block scales
 
   const int b = blockIdx.x;
+  int bb = b;   // the block of the sorted layout this workgroup computes
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar loop control
   const int r16 = lane & 15, kq = lane >> 4;
@@ -120,16 +121,19 @@ __global__ void __launch_bounds__(512) expert_ffn_decode_kernel(
   // ---- the block: its expert e (-1 past the used rows) and its 16 sorted rows -> srow_s
   int e;
   if (!kAlign) {
-    e = block_expert[b];
+    // the used blocks in reverse, walked per XCD, as in the align branch below
+    const int nu = min(al.num_padded[0] / 16, (int)gridDim.x);
+    bb = b < nu ? nu - 1 - xcd_tile(b, nu) : b;
+    e = block_expert[bb];
     if (e < 0) return;
-    if (tid < 16) srow_s[tid] = sorted[b * 16 + tid];
+    if (tid < 16) srow_s[tid] = sorted[bb * 16 + tid];
   } else {
     // The layout of the align call, derived here from topk_ids: per-expert counts
     // (LDS atomics; counts do not depend on their order), each expert's segment padded
     // to 16 rows in ascending expert order, then the block's rows = the entries of its
     // expert ranked 16 (b - first block) .. + 15 in flat-slot order (ballots), padding
     // rows = the sentinel. Entry s = 512 j + tid is held by thread tid.
-    __shared__ int e_s;
+    __shared__ int e_s, bb_s;
     int* cnt_l = reinterpret_cast<int*>(big);   // [256]
     int* pad_l = cnt_l + 256;                   // [256] first row of each expert
     int* wc_l = pad_l + 256;                    // [8][8] entries of e per (j, wavefront)
@@ -159,6 +163,11 @@ __global__ void __launch_bounds__(512) expert_ffn_decode_kernel(
         if (lane >= o) inc += n;
       }
       const int total = __shfl(inc, kWave - 1, kWave);
+      // the used blocks in reverse, walked per XCD: the shared expert's blocks (the last
+      // ones) share one XCD's L2, the one that takes the extra block when 8 does not
+      // divide their number
+      const int nu = total / 16;
+      const int bp = b < nu ? nu - 1 - xcd_tile(b, nu) : b;
       int run = inc - sum;
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
@@ -170,11 +179,12 @@ __global__ void __launch_bounds__(512) expert_ffn_decode_kernel(
             al.offsets[ex] = run;
           }
         }
-        if (pc[u] > 0 && b * 16 >= run && b * 16 < run + pc[u]) e_s = ex;
+        if (pc[u] > 0 && bp * 16 >= run && bp * 16 < run + pc[u]) e_s = ex;
         run += pc[u];
       }
       if (lane == 0) {
-        if (b * 16 >= total) e_s = -1;
+        bb_s = bp;
+        if (bp * 16 >= total) e_s = -1;
         if (b == 0) {
           al.offsets[al.E1] = total;
           al.num_padded[0] = total;
@@ -183,8 +193,9 @@ __global__ void __launch_bounds__(512) expert_ffn_decode_kernel(
     }
     __syncthreads();
     e = e_s;
+    bb = bb_s;
     if (e >= 0) {
-      const int first = b * 16 - pad_l[e];   // rank of the block's first row within e
+      const int first = bb * 16 - pad_l[e];   // rank of the block's first row within e
       const uint64_t lower = (1ull << lane) - 1ull;
       uint64_t m[kJ];
 #pragma unroll
@@ -209,8 +220,8 @@ __global__ void __launch_bounds__(512) expert_ffn_decode_kernel(
       }
     }
     __syncthreads();
-    if (tid < 16) sorted[b * 16 + tid] = srow_s[tid];
-    if (tid == 0) block_expert[b] = e;
+    if (tid < 16) sorted[bb * 16 + tid] = srow_s[tid];
+    if (tid == 0) block_expert[bb] = e;
     if (e < 0) return;
   }
   __syncthreads();
@@ -226,7 +237,7 @@ __global__ void __launch_bounds__(512) expert_ffn_decode_kernel(
   const int nq = NT * nchunks;
   // the blocks of one expert (the shared expert's, at decode) start their K chunks at
   // different offsets, so that they do not all read the same lines at the same time
-  const int rot1 = b % nchunks;
+  const int rot1 = bb % nchunks;
   auto batch_load = [&](int q, u32x4 (&L)[16]) __attribute__((always_inline)) {
     const int n = q / nchunks, c = (q - n * nchunks + rot1) % nchunks;
     const bool in = q < nq;
@@ -341,7 +352,7 @@ __global__ void __launch_bounds__(512) expert_ffn_decode_kernel(
   const int n_my = (ng - wv + 7) >> 3;   // groups wv, wv + 8, ... below ng
   // the wavefront's i-th group is its list's (i + rot3)-th, rotated per block as in phase 1;
   // i >= n_my maps past the end (an empty load, no stores)
-  const int rot3 = n_my > 0 ? b % n_my : 0;
+  const int rot3 = n_my > 0 ? bb % n_my : 0;
   auto group_of = [&](int i) __attribute__((always_inline)) { return i < n_my ? wv + 8 * ((i + rot3) % n_my) : ng; };
   const uint8_t* w2e = w2 + (size_t)e * H * I;
   const float* s2e = s2 + (size_t)e * H;
@@ -389,7 +400,7 @@ __global__ void __launch_bounds__(512) expert_ffn_decode_kernel(
       amax = fmaxf(amax, fabsf(av[m]));
     }
     // the float32 product also goes to the workspace (sorted-row order), where the split path keeps it
-    float* arow = a_out + (size_t)(b * 16 + r) * I + part * C;
+    float* arow = a_out + (size_t)(bb * 16 + r) * I + part * C;
 #pragma unroll
     for (int m = 0; m < C; m += 2) *reinterpret_cast<float2*>(arow + m) = make_float2(av[m], av[m + 1]);
     const float wgt = wgt_s[r];
@@ -515,12 +526,13 @@ bool expert_ffn_decode_align_supported(int T, int K1) { return (size_t)T * K1 <=
 // outputs (T*K1 <= kAlignMaxN).
 hipError_t launch_expert_ffn_decode(const uint8_t* xq, const float* sx, const uint8_t* w13,
                                     const float* s13, const uint8_t* w2, const float* s2, bool block,
-                                    int32_t* sorted, int32_t* block_expert, const AlignOut* align,
-                                    const float* topk_w, float* a_out, uint16_t* slot_out, int T,
-                                    int H, int I, int E1, int K1, hipStream_t stream) {
+                                    int32_t* sorted, int32_t* block_expert, const int32_t* num_padded,
+                                    const AlignOut* align, const float* topk_w, float* a_out,
+                                    uint16_t* slot_out, int T, int H, int I, int E1, int K1,
+                                    hipStream_t stream) {
   const int P_max = (int)sorted_capacity(T, K1, E1, 16);
   const dim3 grid(P_max / 16), blk(512);
-  const AlignOut al = align ? *align : AlignOut{nullptr, nullptr, nullptr, nullptr, E1};
+  const AlignOut al = align ? *align : AlignOut{nullptr, nullptr, nullptr, const_cast<int32_t*>(num_padded), E1};
 #define SRMOE_EFD(B, N, A)                                                                          \
   hipLaunchKernelGGL((expert_ffn_decode_kernel<B, N, A>), grid, blk, 0, stream, xq, sx, w13, s13, w2, \
                      s2, sorted, block_expert, al, topk_w, a_out, slot_out, T, H, K1)
