@@ -229,17 +229,16 @@ __global__ void __launch_bounds__(512) expert_ffn_decode_kernel(
   // ---- phase 1 prologue: per-row and per-column data, x rows into LDS, first weight batch
   const uint8_t* w13e = w13 + (size_t)e * 2 * I * H;
   const int tile0 = wv * NT;   // first of the wavefront's 16-row tiles of w13[e]
-  // Batch q = (tile pass q / nchunks, K chunk (q + rot1) % nchunks): row r of the tile is load r, at
+  // Batch q = (tile pass q / nchunks, K chunk q % nchunks): row r of the tile is load r, at
   // scalar offset r * H; lane l takes bytes 16 l .. 16 l + 15 of the chunk (an out-of-range
   // offset, read as zero, past the end of a row). Batches past the last get a zero-length
   // resource.
   const int nchunks = (H + kRunK - 1) / kRunK;
   const int nq = NT * nchunks;
-  // the blocks of one expert (the shared expert's, at decode) start their K chunks at
-  // different offsets, so that they do not all read the same lines at the same time
-  const int rot1 = bb % nchunks;
+  // (the blocks of one expert, the shared expert's at decode, run on one XCD and walk
+  // the same K chunks in step, so that its L2 serves the lines they share)
   auto batch_load = [&](int q, u32x4 (&L)[16]) __attribute__((always_inline)) {
-    const int n = q / nchunks, c = (q - n * nchunks + rot1) % nchunks;
+    const int n = q / nchunks, c = q - n * nchunks;
     const bool in = q < nq;
     const __amdgpu_buffer_rsrc_t r =
         slice_rsrc(w13e + (in ? (size_t)16 * (tile0 + n) * H : 0), in ? (uint32_t)(16 * H) : 0u);
@@ -300,7 +299,7 @@ __global__ void __launch_bounds__(512) expert_ffn_decode_kernel(
 #pragma unroll
   for (int n = 0; n < NT; ++n) acc[n] = zero4;
   auto process = [&](u32x4 (&L)[16], int q) __attribute__((always_inline)) {
-    const int n = q / nchunks, c = (q - n * nchunks + rot1) % nchunks;
+    const int n = q / nchunks, c = q - n * nchunks;
     const int srow13 = (16 * (tile0 + n)) / kGroup;   // the tile's block row of w13[e]'s scales
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
@@ -330,7 +329,7 @@ __global__ void __launch_bounds__(512) expert_ffn_decode_kernel(
       __builtin_amdgcn_sched_barrier(0);
     }
     asm volatile("" : "+v"(cur));   // the batch's MFMAs stay in the batch (not sunk into the next)
-    if (q < nq && q - n * nchunks == nchunks - 1) {   // the pass's last batch (whatever its chunk)
+    if (q < nq && c == nchunks - 1) {   // the pass's last batch
 #pragma unroll
       for (int m = 0; m + 1 < NT; ++m) acc[m] = acc[m + 1];
       acc[NT - 1] = cur;
@@ -350,10 +349,8 @@ __global__ void __launch_bounds__(512) expert_ffn_decode_kernel(
   // ---- phase 3 prologue: the wavefront's first w2 group starts loading now
   const int ng = H / 64;
   const int n_my = (ng - wv + 7) >> 3;   // groups wv, wv + 8, ... below ng
-  // the wavefront's i-th group is its list's (i + rot3)-th, rotated per block as in phase 1;
-  // i >= n_my maps past the end (an empty load, no stores)
-  const int rot3 = n_my > 0 ? bb % n_my : 0;
-  auto group_of = [&](int i) __attribute__((always_inline)) { return i < n_my ? wv + 8 * ((i + rot3) % n_my) : ng; };
+  // the wavefront's i-th group; i >= n_my maps past the end (an empty load, no stores)
+  auto group_of = [&](int i) __attribute__((always_inline)) { return i < n_my ? wv + 8 * i : ng; };
   const uint8_t* w2e = w2 + (size_t)e * H * I;
   const float* s2e = s2 + (size_t)e * H;
   // the wavefront's i-th group: its 64 rows of w2[e] and their 64 channel scales
