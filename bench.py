@@ -3,16 +3,21 @@
 
 One step = one pass of the whole layer (route + shared append, align/sort/pad,
 the fused FP8 expert FFN over all 9 slots, weighted combine) over one batch of
-synthetic input already resident in HBM. The default workload is the TP8
-decode shard: T=64 tokens, H=5120, 160 routed + 1 shared experts, I=192,
-top-8 + shared. Two independent weight sets (2 x 475 MB) are cycled so the
-weights stream from HBM rather than from the 256 MB last-level cache.
+synthetic input already resident in HBM, through moe_layer_forward. The line's
+value is the TP8 decode shard: T=64 tokens, H=5120, 160 routed + 1 shared
+experts, I=192, top-8 + shared. The default run adds a "prefill" record for the
+4,096-token chunk of the same shard (the prefill half of the metric). Two
+independent weight sets (2 x 475 MB) are cycled so the weights stream from HBM
+rather than from the 256 MB last-level cache.
 
-Prints one JSON line: the layer's tokens/s and time per step, the roofline of the
-dominant expert kernel (its algorithmic bytes over its measured launch time, against
-8 TB/s), per-stage times, the router gate, the layer from x, the QK-Norm + RoPE step,
-the fused-vs-unfused comparison and the CPU oracle's rate. `--gpus` above 1 is
-refused: the library runs on one GPU.
+Each record carries tokens/s and time per step, per-stage times (HIP events that
+the library records between its launches, moe_layer_forward_staged), the roofline
+of the dominant kernel (its algorithmic flops or bytes over its measured launch
+time; the bound follows its arithmetic intensity: the fp8 MFMA peak above the
+ridge, 8 TB/s below), the layer's fp8 and HBM fractions, the four separate calls,
+the fused-vs-unfused comparison and the CPU oracle's rate on a token sample. The
+decode record also times the router gate, the layer from x and the QK-Norm + RoPE
+step. `--gpus` above 1 is refused: the library runs on one GPU.
 """
 from __future__ import annotations
 
@@ -46,11 +51,11 @@ DEFAULT_BLOCK_M = {"decode": 16, "prefill": 128, "prefill16k_zipf": 128, "unshar
 # of known size. The summary records a hash of the kernel's source files; when the sources
 # have changed since, the figure is null.
 TRAFFIC_PROFILES = {
-    ("decode", 16): ("profiles/expert_ffn_decode_T64_hbm_traffic.txt",
-                     ["shared_routed_expert_amd/csrc/ffn_expert_decode.hip",
-                      "shared_routed_expert_amd/csrc/common.hpp"]),
-    ("prefill", 128): ("profiles/gate_up_tile_prefill_T4096_hbm_traffic.txt",
-                       ["shared_routed_expert_amd/csrc/ffn_tile.hip", "shared_routed_expert_amd/csrc/common.hpp"]),
+    ("decode", "experts"): ("profiles/expert_ffn_decode_T64_hbm_traffic.txt",
+                            ["shared_routed_expert_amd/csrc/ffn_expert_decode.hip",
+                             "shared_routed_expert_amd/csrc/common.hpp"]),
+    ("prefill", "gate_up"): ("profiles/gate_up_tile_prefill_T4096_hbm_traffic.txt",
+                             ["shared_routed_expert_amd/csrc/ffn_tile.hip", "shared_routed_expert_amd/csrc/common.hpp"]),
 }
 
 
@@ -63,8 +68,8 @@ def source_hash(files):
     return h.hexdigest()[:16]
 
 
-def traffic_from_profile(workload, block_m):
-    entry = TRAFFIC_PROFILES.get((workload, block_m))
+def traffic_from_profile(workload, kernel):
+    entry = TRAFFIC_PROFILES.get((workload, kernel))
     if entry is None:
         return None
     path, files = entry
@@ -93,7 +98,27 @@ def copy_calibration(mib: int, reps: int):
     print(json.dumps({"copy_calibration_bytes_read": n, "bytes_written": n, "reps": reps}), flush=True)
 
 
-def cpu_baseline(inp, budget_s: float):
+CPU_SAMPLE_TOKENS = {"decode": 64, "prefill": 128, "prefill16k_zipf": 128, "unsharded_block": 16, "tiny": 16}
+
+
+def host_cpu():
+    """The host's logical CPU count, the process's affinity and the CPU model."""
+    model = ""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    try:
+        aff = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):  # pragma: no cover
+        aff = None
+    return {"cpu_count": os.cpu_count(), "affinity": aff, "cpu_model": model}
+
+
+def cpu_baseline(inp, budget_s: float, n_tokens: int):
     """The CPU oracle (fused form, as it stands) on a bounded token sample."""
     import numpy as np
     import oracle
@@ -105,7 +130,7 @@ def cpu_baseline(inp, budget_s: float):
         threads = os.cpu_count()
     c = inp.cfg
     x = f32_from_bf16_bits(inp.x_bf16)
-    n = min(c.T, 64)
+    n = min(c.T, n_tokens)
     times = []
     t_all = time.perf_counter()
     # at least 3 runs and about 10 s of work, within the budget
@@ -116,9 +141,11 @@ def cpu_baseline(inp, budget_s: float):
         oracle.moe_fused(x, inp.logits, c.K, inp.w13_q, inp.s13, inp.w2_q, inp.s2, tokens=tok)
         times.append(time.perf_counter() - t0)
     med = statistics.median(times)
-    return {"value": n / med, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"first {n} tokens of the {c.name} batch (routing over all {c.T}), float64 numpy "
-                      f"oracle, median of {len(times)} runs ({med:.2f} s each)"}
+    rec = {"value": n / med, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+           "sample": f"first {n} tokens of the {c.name} batch (routing over all {c.T}), float64 numpy "
+                     f"oracle, median of {len(times)} runs ({med:.2f} s each)"}
+    rec.update(host_cpu())
+    return rec
 
 
 def router_timing(inp, x, steps):
@@ -280,40 +307,65 @@ def fusion_ab(cfg, bm, x, logits, weights, fused, steps):
     return res
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="decode", choices=sorted(WORKLOAD_TEXT))
-    ap.add_argument("--block-m", type=int, default=None)
-    ap.add_argument("--weight-sets", type=int, default=2)
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-budget", type=float, default=30.0)
-    ap.add_argument("--no-fusion-ab", action="store_true", help="skip the fused-vs-unfused comparison")
-    ap.add_argument("--copy-calib-mib", type=int, default=0,
-                    help="only run a plain copy of this many MiB (counter calibration) and exit")
-    args = ap.parse_args()
+RIDGE = FP8_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)   # flop/B where the fp8 MFMA and HBM bounds meet
 
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: the library has no multi-GPU path (under TP8 each GPU "
-              "runs this layer on its 192-wide slice of every expert and an all-reduce sums the "
-              "partial outputs; that exchange is not built).", file=sys.stderr)
-        sys.exit(2)
 
+def stage_work(stage, cfg, active, active_routed, P):
+    """Algorithmic (flops, bytes) of one launch of a stage of moe_layer_forward: the weights and
+    scales of the experts it serves read once, the activations it needs read once and the results
+    it hands on written once (in their smallest form: FP8 codes plus one scale per row). Not
+    counted: padding rows, re-reads, and the slot rows of the routed experts (the slot buffer's
+    round trip is an overhead of the design, not work of the method)."""
+    T, H, I, E, K, K1 = cfg.T, cfg.H, cfg.I, cfg.E, cfg.K, cfg.K1
+    blk = cfg.scale_mode == "block128"
+    s13 = (2 * I // 128) * (H // 128) * 4 if blk else 2 * I * 4
+    s2 = (H // 128) * (I // 128) * 4 if blk else H * 4
+    gx = H // 128 if blk else 1
+    ga = I // 128 if blk else 1
+    rows = T * K1
+    if stage == "front":        # logits in, routing tables out; x in, x codes + scales out
+        return 0.0, T * E * 4 + T * K1 * 8 + T * H * 2 + T * (H + 4 * gx)
+    if stage == "align":
+        return 0.0, rows * 4 + P * 4
+    if stage == "experts":      # the whole expert FFN of a decode batch, slot rows out
+        return rows * 6.0 * H * I, active * (3 * I * H + s13 + s2) + T * (H + 4 * gx) + rows * H * 2
+    if stage == "gate_up":      # w13 + x codes in, the SwiGLU rows out (as FP8 codes + scales)
+        return rows * 4.0 * H * I, active * (2 * I * H + s13) + T * (H + 4 * gx) + rows * (I + 4 * ga)
+    if stage == "quant_a":
+        return 0.0, rows * (I * 4 + I + 4 * ga + 4)
+    if stage == "down_routed":  # w2 of the routed experts + the routed SwiGLU rows in
+        return T * K * 2.0 * H * I, active_routed * (I * H + s2) + T * K * (I + 4 * ga)
+    if stage == "down_shared_combine":   # the shared expert's down GEMM and the combine: out written
+        return T * 2.0 * H * I, (I * H + s2) + T * (I + 4 * ga) + T * H * 2
+    if stage == "combine":
+        return 0.0, rows * H * 2 + T * H * 2
+    return None
+
+
+def roofline_of(flops, nbytes, us):
+    """Bound from the arithmetic intensity: the fp8 MFMA peak above the ridge, HBM below."""
+    if flops / max(nbytes, 1) > RIDGE:
+        ach = flops / (us * 1e-6) / 1e12
+        return {"bound": "mfma", "achieved": round(ach, 2), "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(ach / FP8_PEAK_TFLOPS, 4)}
+    ach = nbytes / (us * 1e-6) / 1e9
+    return {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(ach / HBM_PEAK_GBS, 4)}
+
+
+def measure(name, args, with_extras):
+    """One workload: the layer through moe_layer_forward, timed over args.steps steps after
+    args.warmup, its stages timed with events recorded by the library between its launches,
+    the dominant kernel's roofline, the four separate calls, and the CPU oracle."""
     import numpy as np
     import torch
     from workloads import CONFIGS, generate
     from shared_routed_expert_amd import FusedMoE, DeviceWeights
 
-    if args.copy_calib_mib:
-        copy_calibration(args.copy_calib_mib, max(args.steps, 1))
-        return
-
-    cfg = CONFIGS[args.workload]
-    bm = args.block_m or DEFAULT_BLOCK_M[args.workload]
+    cfg = CONFIGS[name]
+    bm = args.block_m or DEFAULT_BLOCK_M[name]
     dev = "cuda:0"
-    log(f"bench: generating {args.workload} inputs ({args.weight_sets} weight sets)")
+    log(f"bench: generating {name} inputs ({args.weight_sets} weight sets)")
     sets = [generate(cfg, weight_set=j) for j in range(args.weight_sets)]
     inp = sets[0]
     weights = [DeviceWeights.from_numpy(s.w13_q, s.s13, s.w2_q, s.s2, device=dev) for s in sets]
@@ -330,12 +382,12 @@ def main():
     def step_four_calls(i):   # the same layer as the four separate C calls
         layer.forward(x, logits, weights[i % len(weights)], 1.0, stream)
 
-    log(f"bench: warmup {args.warmup} steps")
+    log(f"bench: {name}: warmup {args.warmup} steps")
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
 
-    # Timed region 1: the whole layer, K steps.
+    # Timed region: the whole layer, K steps, bracketed by synchronisations.
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -346,10 +398,10 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = ev0.elapsed_time(ev1) / args.steps
-    log(f"bench: {ms_per_step * 1e3:.1f} us/step on the GPU, {wall * 1e6 / args.steps:.1f} us/step wall-clock")
+    log(f"bench: {name}: {ms_per_step * 1e3:.1f} us/step on the GPU, {wall * 1e6 / args.steps:.1f} us/step "
+        f"wall-clock")
 
-    # Per-step durations of the same layer call (events around each step), for the
-    # median and the 10th / 90th percentiles.
+    # Per-step durations of the same call (events around each step): median and 10th / 90th percentiles.
     sev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
     sev[0].record(stream)
@@ -360,7 +412,24 @@ def main():
     step_us = sorted(1e3 * sev[i].elapsed_time(sev[i + 1]) for i in range(args.steps))
     pct = lambda q: step_us[min(len(step_us) - 1, int(q * (len(step_us) - 1) + 0.5))]
 
-    # The same K steps through the four separate calls, for comparison.
+    # The same layer call with events recorded by the library between its launches (same
+    # stream, same kernels): each stage's average duration, the dominant kernel's included.
+    nev = 12
+    sevs = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(args.steps)]
+    for evl in sevs:
+        for e in evl:
+            e.record(stream)   # creates the underlying HIP events
+    torch.cuda.synchronize()
+    names = None
+    for i in range(args.steps):
+        names = layer.forward_staged(x, logits, weights[i % len(weights)], 1.0, sevs[i], stream)
+    torch.cuda.synchronize()
+    stage_us = {n: 1e3 * statistics.mean(sevs[i][j].elapsed_time(sevs[i][j + 1]) for i in range(args.steps))
+                for j, n in enumerate(names)}
+
+    # The four separate calls, warmed up first.
+    for i in range(args.warmup):
+        step_four_calls(i)
     torch.cuda.synchronize()
     ev0.record(stream)
     for i in range(args.steps):
@@ -369,70 +438,32 @@ def main():
     torch.cuda.synchronize()
     four_ms = ev0.elapsed_time(ev1) / args.steps
 
-    # Timed region 2: the same steps with HIP events between the stages (same stream),
-    # giving each stage's average duration, the dominant kernel's included.
-    ffn_names = layer.ffn_stage_names()
-    names = ["route", "align"] + ffn_names + ["combine"]
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    for i in range(args.steps):
-        e = evs[i]
-        W = weights[i % len(weights)]
-        e[0].record(stream)
-        layer.route(logits, 1.0, stream)
-        e[1].record(stream)
-        layer.align(stream)
-        e[2].record(stream)
-        marks = iter(e[3:3 + len(ffn_names)])
-        layer.ffn_stages(x, W, stream, between=lambda _n: next(marks).record(stream))
-        layer.combine(stream)
-        e[len(names)].record(stream)
-    torch.cuda.synchronize()
-    stage_us = {n: 1e3 * statistics.mean(evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(args.steps))
-                for j, n in enumerate(names)}
-
     counts = layer.expert_counts.cpu().numpy()
     active = int((counts > 0).sum())
+    active_routed = int((counts[:cfg.E] > 0).sum())
+    P = int(layer.num_padded.item())
     T, H, I, E1, K1 = cfg.T, cfg.H, cfg.I, cfg.E1, cfg.K1
     blk = cfg.scale_mode == "block128"
     s13_bytes = (2 * I // 128) * (H // 128) * 4 if blk else 2 * I * 4
     s2_bytes = (H // 128) * (I // 128) * 4 if blk else H * 4
-    if "experts" in stage_us:
-        # Algorithmic bytes of the one-kernel expert FFN: each activated expert's W13 (2*I*H fp8),
-        # W2 (I*H fp8) and their scales read once, x_q (T*H fp8) read once, and the weighted
-        # bf16 slot rows (T*K1*H*2) written once.
-        dom = "experts"
-        dom_bytes = active * (3 * I * H + s13_bytes + s2_bytes) + T * H + T * K1 * H * 2
-    else:
-        # Algorithmic bytes of the gate_up kernel: each activated expert's W13 (2*I*H fp8) and
-        # its scales read once, plus the quantised activations x_q (T*H fp8) read once.
-        dom = "gate_up"
-        dom_bytes = active * (2 * I * H + s13_bytes) + T * H
-    achieved = dom_bytes / (stage_us[dom] * 1e-6) / 1e9
+    dom = max(stage_us, key=stage_us.get)
+    work = stage_work(dom, cfg, active, active_routed, P)
+    if work is None:   # a stage made of several kernels (the split FFN path)
+        dom = max((n for n in stage_us if stage_work(n, cfg, active, active_routed, P)), key=stage_us.get)
+        work = stage_work(dom, cfg, active, active_routed, P)
+    flops_k, bytes_k = work
+    roof = roofline_of(flops_k, bytes_k, stage_us[dom])
+    roof.update({"kernel": dom, "traffic": traffic_from_profile(name, dom), "alg_bytes_per_launch": int(bytes_k),
+                 "alg_flops_per_launch": int(flops_k), "avg_launch_us": round(stage_us[dom], 2),
+                 "timing": "HIP events recorded by moe_layer_forward_staged around the launch"})
     layer_bytes = active * (3 * I * H + s13_bytes + s2_bytes) + T * H * 2 * 2 + T * cfg.E * 4 + T * K1 * 8
     flops = T * K1 * 6 * H * I
     step_s = ms_per_step * 1e-3
-
-    result = {
-        "metric": "fused MoE layer tokens/s + % fp8 MFMA peak (prefill) / % HBM BW (decode)",
-        "value": round(T / step_s, 1),
-        "unit": "tokens/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 5),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "fp8e4m3 (fp32 accumulate)",
-        "data": "synthetic (seeded; random-init fp8 expert weights of the GLM4-MoE TP8 shard shape)",
-        "config": {"workload": WORKLOAD_TEXT[args.workload], "T": T, "H": H, "I": I, "routed_experts": cfg.E,
-                   "shared_experts": 1, "top_k": cfg.K, "slots": K1, "block_m": bm,
-                   "weight_sets_cycled": len(weights), "active_experts": active, "parallelism": "single GPU"},
-        "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1),
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": traffic_from_profile(args.workload, bm), "alg_bytes_per_launch": dom_bytes,
-                     "avg_launch_us": round(stage_us[dom], 2)},
+    rec = {
+        "workload": WORKLOAD_TEXT[name], "T": T, "H": H, "I": I, "routed_experts": cfg.E, "shared_experts": 1,
+        "top_k": cfg.K, "slots": K1, "block_m": bm, "weight_sets_cycled": len(weights), "active_experts": active,
+        "tokens_per_s": round(T / step_s, 1), "ms_per_step": round(ms_per_step, 5),
+        "roofline": roof,
         "layer": {"alg_bytes": layer_bytes, "alg_GBps": round(layer_bytes / step_s / 1e9, 1),
                   "hbm_frac": round(layer_bytes / step_s / 1e9 / HBM_PEAK_GBS, 4),
                   "alg_TFLOPs": round(flops / step_s / 1e12, 2),
@@ -441,21 +472,82 @@ def main():
                                          / (pct(0.5) * 1e-6), 4),
                   "step_us_p10_p50_p90": [round(pct(0.1), 2), round(pct(0.5), 2), round(pct(0.9), 2)],
                   "stage_us": {k: round(v, 2) for k, v in stage_us.items()},
+                  "stage_roofline": {k: roofline_of(*stage_work(k, cfg, active, active_routed, P), v)["frac"]
+                                     for k, v in stage_us.items() if stage_work(k, cfg, active, active_routed, P)},
                   "entry_point": "moe_layer_forward",
                   "four_call_ms_per_step": round(four_ms, 5)},
     }
-    log("bench: router gate (graph replays)")
-    result["router_gate"] = router_timing(inp, x, args.steps)
-    log("bench: routing and the layer from x (graph replays)")
-    result["from_x"] = from_x_timing(inp, x, layer, weights, args.steps)
-    log("bench: QK-Norm + RoPE, fused and unfused (graph replays)")
-    result["qk_norm_rope"] = qk_norm_rope_timing(args.steps)
+    if with_extras:
+        log("bench: router gate (graph replays)")
+        rec["router_gate"] = router_timing(inp, x, args.steps)
+        log("bench: routing and the layer from x (graph replays)")
+        rec["from_x"] = from_x_timing(inp, x, layer, weights, args.steps)
+        log("bench: QK-Norm + RoPE, fused and unfused (graph replays)")
+        rec["qk_norm_rope"] = qk_norm_rope_timing(args.steps)
     if not args.no_fusion_ab:
-        log("bench: fused vs unfused layer (graph replays)")
-        result["fusion_ab"] = fusion_ab(cfg, bm, x, logits, weights, layer, args.steps)
+        log(f"bench: {name}: fused vs unfused layer (graph replays)")
+        rec["fusion_ab"] = fusion_ab(cfg, bm, x, logits, weights, layer, args.steps)
+    del weights, layer
+    torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
-        log("bench: timing the CPU oracle")
-        result["cpu_baseline"] = cpu_baseline(inp, args.cpu_budget)
+        log(f"bench: {name}: timing the CPU oracle")
+        rec["cpu_baseline"] = cpu_baseline(inp, args.cpu_budget, CPU_SAMPLE_TOKENS.get(name, 64))
+    return rec
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="default", choices=["default"] + sorted(WORKLOAD_TEXT),
+                    help="default: the decode workload (the line's value) plus the prefill record")
+    ap.add_argument("--block-m", type=int, default=None)
+    ap.add_argument("--weight-sets", type=int, default=2)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=30.0)
+    ap.add_argument("--no-fusion-ab", action="store_true", help="skip the fused-vs-unfused comparison")
+    ap.add_argument("--copy-calib-mib", type=int, default=0,
+                    help="only run a plain copy of this many MiB (counter calibration) and exit")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the library has no multi-GPU path (under TP8 each GPU "
+              "runs this layer on its 192-wide slice of every expert and an all-reduce sums the "
+              "partial outputs; that exchange is not built).", file=sys.stderr)
+        sys.exit(2)
+
+    if args.copy_calib_mib:
+        copy_calibration(args.copy_calib_mib, max(args.steps, 1))
+        return
+
+    head = "decode" if args.workload == "default" else args.workload
+    rec = measure(head, args, with_extras=True)
+    result = {
+        "metric": "fused MoE layer tokens/s + % fp8 MFMA peak (prefill) / % HBM BW (decode)",
+        "value": rec["tokens_per_s"],
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": rec["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8e4m3 (fp32 accumulate)",
+        "data": "synthetic (seeded; random-init fp8 expert weights of the GLM4-MoE TP8 shard shape)",
+        "config": {k: rec[k] for k in ("workload", "T", "H", "I", "routed_experts", "shared_experts", "top_k",
+                                       "slots", "block_m", "weight_sets_cycled", "active_experts")},
+        "roofline": rec["roofline"],
+    }
+    result["config"]["parallelism"] = "single GPU"
+    for k in ("layer", "router_gate", "from_x", "qk_norm_rope", "fusion_ab", "cpu_baseline"):
+        if k in rec:
+            result[k] = rec[k]
+    if args.workload == "default":
+        # the prefill half of the metric: the 4,096-token chunk (the pages' input length)
+        pre = measure("prefill", args, with_extras=False)
+        result["prefill"] = pre
     print(json.dumps(result), flush=True)
 
 

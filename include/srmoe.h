@@ -229,12 +229,19 @@ int moe_ffn_down(const uint8_t* w2, const float* s2, int scale_mode, int T, int 
 /* ---------------------------------------------------------------------------
  * Step 4: weighted combine (Novita AI section 1: the experts' outputs are
  * weighted and aggregated). out[t,:] = bf16( sum_{k=0..K1-1} slot_out[t*K1+k,:] )
- * accumulated in float32 in slot order 0..K1-1, where slot_out (already scaled
- * by the routing weights) is the one moe_fused_ffn left in `workspace`.
+ * accumulated in float32 in slot order 0..K1-1, where slot_out is the one
+ * moe_fused_ffn left in `workspace`.
+ *   topk_w [T,K1] float32, the routing weights of step 1 (may be NULL). The
+ *          weighting itself happens in moe_fused_ffn's down GEMM, which stores
+ *          each slot row as bf16(topk_w[s] * y): the weight is one factor of the
+ *          row's dequantisation scale there, so the combine is a plain sum and the
+ *          weighted rows are rounded once. The argument is part of the call so
+ *          that the weighting can move between the two kernels without an ABI
+ *          change; the current kernels do not read it.
  *   out [T,H] bf16 out.
  * ------------------------------------------------------------------------- */
-int moe_combine(int T, int K1, int H, const void* workspace, size_t ws_bytes, uint16_t* out,
-                void* stream);
+int moe_combine(const float* topk_w, int T, int K1, int H, const void* workspace, size_t ws_bytes,
+                uint16_t* out, void* stream);
 
 /* ---------------------------------------------------------------------------
  * The whole layer in one call: steps 1-4 with the arguments of the four calls
@@ -256,6 +263,22 @@ int moe_layer_forward(const uint16_t* x, const float* logits, const uint8_t* w13
                       int32_t* expert_offsets, int32_t* num_padded, void* align_ws,
                       size_t align_ws_bytes, void* ffn_ws, size_t ffn_ws_bytes, uint16_t* out,
                       void* stream);
+
+/* Measurement form of moe_layer_forward: the same launches and outputs, with caller-created
+ * hipEvent_t events (host array `events` of n_events handles) recorded on `stream` between
+ * the layer's stages: events[0] before the first launch, events[i] after stage i, for as
+ * many stages as there are events. stage_names (host, may be NULL) receives in entry i - 1
+ * a static name for stage i ("front", "align", "experts", "gate_up", "quant_a",
+ * "down_routed", "down_shared_combine", "combine", ...); *n_recorded (host, may be NULL) the number of events
+ * recorded. The elapsed time between events i - 1 and i is stage i's share of the layer. */
+int moe_layer_forward_staged(const uint16_t* x, const float* logits, const uint8_t* w13, const float* s13,
+                             const uint8_t* w2, const float* s2, int scale_mode, int T, int H, int I, int E,
+                             int K, float shared_weight, int block_m, int32_t* topk_ids, float* topk_w,
+                             int32_t* sorted_slot_ids, int32_t* block_expert, int32_t* expert_counts,
+                             int32_t* expert_offsets, int32_t* num_padded, void* align_ws,
+                             size_t align_ws_bytes, void* ffn_ws, size_t ffn_ws_bytes, uint16_t* out,
+                             void* stream, void* const* events, int n_events, const char** stage_names,
+                             int* n_recorded);
 
 /* ---------------------------------------------------------------------------
  * Attention side of the same model: the per-head QK norm fused with the rotary
@@ -301,6 +324,14 @@ size_t moe_ffn_workspace_bytes(int T, int H, int I, int E1, int K1, int block_m,
  * SRMOE_ERR_UNSUPPORTED for bad shapes. */
 int moe_ffn_workspace_offsets(int T, int H, int I, int E1, int K1, int block_m, int scale_mode,
                               size_t* out /* host, 8 entries */);
+/* Bytes of ONE device workspace that serves moe_align_by_expert, moe_fused_ffn (and its
+ * stages) and moe_combine for these sizes: the larger of moe_align_workspace_bytes and
+ * moe_ffn_workspace_bytes (0 for an unsupported shape). The same buffer may be passed to all
+ * of them, and as both align_ws and ffn_ws of moe_layer_forward: align's scratch is dead
+ * once it returns, before the FFN writes there (calls on one stream run in order). */
+size_t moe_workspace_bytes(int T, int H, int I, int E1, int K1, int block_m, int scale_mode);
+/* Text of a status code (static storage). srmoe_status_string is the same function. */
+const char* moe_status_string(int status);
 const char* srmoe_status_string(int status);
 int srmoe_last_hip_error(void); /* hipError_t of this thread's last failed launch, 0 if none */
 

@@ -40,12 +40,16 @@ def _load():
         "moe_ffn_down": ([P, P, I, I, I, I, I, I, I, P, P, P, P, P, Z, P], I),
         "moe_ffn_experts": ([P, P, P, P, I, I, I, I, I, I, I, P, P, P, P, P, Z, P], I),
         "moe_ffn_experts_one_kernel": ([I, I, I], I),
-        "moe_combine": ([I, I, I, P, Z, P, P], I),
+        "moe_combine": ([P, I, I, I, P, Z, P, P], I),
         "moe_route_topk": ([P, I, I, I, P, P, P], I),
         "moe_router_logits": ([P, P, P, I, I, I, P, P, Z, P], I),
         "moe_router_workspace_bytes": ([I, I, I], Z),
         "moe_combine_unfused": ([I, I, I, P, Z, P, Z, P, P], I),
         "moe_layer_forward": ([P, P, P, P, P, P, I, I, I, I, I, I, F, I, P, P, P, P, P, P, P, P, Z, P, Z, P, P], I),
+        "moe_layer_forward_staged": ([P, P, P, P, P, P, I, I, I, I, I, I, F, I, P, P, P, P, P, P, P, P, Z, P, Z, P,
+                                      P, P, I, P, P], I),
+        "moe_workspace_bytes": ([I, I, I, I, I, I, I], Z),
+        "moe_status_string": ([I], ctypes.c_char_p),
         "moe_qk_norm_rope": ([P, I, I, I, I, I, I, P, P, F, P, P, I, I, P], I),
         "moe_route_from_x": ([P, P, P, I, I, I, I, F, P, P, P, Z, P], I),
         "moe_route_from_x_workspace_bytes": ([I, I, I], Z),
@@ -74,8 +78,8 @@ EXPORTED = ("moe_route_topk_plus_shared", "moe_align_by_expert", "moe_fused_ffn"
             "moe_router_workspace_bytes", "moe_qk_norm_rope", "moe_rope_cos_sin_table", "moe_route_from_x",
             "moe_route_from_x_workspace_bytes", "moe_layer_forward_from_x", "moe_sorted_capacity",
             "moe_align_workspace_bytes", "moe_ffn_workspace_bytes", "moe_ffn_workspace_offsets",
-            "srmoe_status_string",
-            "srmoe_last_hip_error")
+            "srmoe_status_string", "srmoe_last_hip_error", "moe_workspace_bytes", "moe_status_string",
+            "moe_layer_forward_staged")
 
 
 def _ptr(t):
@@ -112,6 +116,14 @@ def moe_align_workspace_bytes(T, K1, E1):
 
 def moe_ffn_workspace_bytes(T, H, I, E1, K1, block_m, scale_mode):
     return lib.moe_ffn_workspace_bytes(T, H, I, E1, K1, block_m, scale_mode)
+
+
+def moe_workspace_bytes(T, H, I, E1, K1, block_m, scale_mode):
+    return lib.moe_workspace_bytes(T, H, I, E1, K1, block_m, scale_mode)
+
+
+def moe_status_string(status):
+    return lib.moe_status_string(status).decode()
 
 
 def moe_ffn_workspace_offsets(T, H, I, E1, K1, block_m, scale_mode):
@@ -178,8 +190,8 @@ def moe_ffn_experts_one_kernel(H, I, block_m):
     return bool(lib.moe_ffn_experts_one_kernel(H, I, block_m))
 
 
-def moe_combine(T, K1, H, workspace, ws_bytes, out, stream=None, check=True):
-    st = lib.moe_combine(T, K1, H, _ptr(workspace), ws_bytes, _ptr(out), _stream(stream))
+def moe_combine(topk_w, T, K1, H, workspace, ws_bytes, out, stream=None, check=True):
+    st = lib.moe_combine(_ptr(topk_w), T, K1, H, _ptr(workspace), ws_bytes, _ptr(out), _stream(stream))
     return _check("moe_combine", st) if check else st
 
 
@@ -216,6 +228,27 @@ def moe_layer_forward(x, logits, w13, s13, w2, s2, scale_mode, T, H, I, E, K, sh
                                _ptr(align_ws), align_ws_bytes, _ptr(ffn_ws), ffn_ws_bytes, _ptr(out),
                                _stream(stream))
     return _check("moe_layer_forward", st) if check else st
+
+
+def moe_layer_forward_staged(x, logits, w13, s13, w2, s2, scale_mode, T, H, I, E, K, shared_weight, block_m,
+                             topk_ids, topk_w, sorted_slot_ids, block_expert, expert_counts, expert_offsets,
+                             num_padded, align_ws, align_ws_bytes, ffn_ws, ffn_ws_bytes, out, events,
+                             stream=None, check=True):
+    """moe_layer_forward with the given torch.cuda.Events (already created: recorded once)
+    recorded between its stages. Returns the list of stage names, one per recorded interval."""
+    n = len(events)
+    ev = (ctypes.c_void_p * max(n, 1))(*[e.cuda_event for e in events])
+    names = (ctypes.c_char_p * max(n, 1))()
+    rec = ctypes.c_int(0)
+    st = lib.moe_layer_forward_staged(_ptr(x), _ptr(logits), _ptr(w13), _ptr(s13), _ptr(w2), _ptr(s2),
+                                      scale_mode, T, H, I, E, K, shared_weight, block_m, _ptr(topk_ids),
+                                      _ptr(topk_w), _ptr(sorted_slot_ids), _ptr(block_expert),
+                                      _ptr(expert_counts), _ptr(expert_offsets), _ptr(num_padded),
+                                      _ptr(align_ws), align_ws_bytes, _ptr(ffn_ws), ffn_ws_bytes, _ptr(out),
+                                      _stream(stream), ev, n, names, ctypes.byref(rec))
+    if check:
+        _check("moe_layer_forward_staged", st)
+    return [names[i].decode() for i in range(max(rec.value - 1, 0))]
 
 
 def moe_qk_norm_rope(qkv, T, num_q_heads, num_kv_heads, head_dim, rotary_dim, neox, q_norm_w, k_norm_w, eps,

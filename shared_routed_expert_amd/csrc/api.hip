@@ -30,7 +30,7 @@ hipError_t launch_combine(const uint16_t*, const uint16_t*, int, int, int, uint1
 bool down_wide_supported(int I);
 hipError_t launch_down_wide_combine(const uint8_t*, const float*, const uint8_t*, const float*, bool,
                                     const int32_t*, const int32_t*, const int32_t*, const float*, uint16_t*,
-                                    uint16_t*, int, int, int, int, int, hipStream_t);
+                                    uint16_t*, int, int, int, int, int, int, hipStream_t);
 hipError_t launch_gate_up_decode(const uint8_t*, const float*, const uint8_t*, const float*, bool,
                                  const int32_t*, const int32_t*, float*, int, int, int, int, int,
                                  hipStream_t);
@@ -155,7 +155,16 @@ const char* srmoe_status_string(int status) {
   }
 }
 
+const char* moe_status_string(int status) { return srmoe_status_string(status); }
+
 int srmoe_last_hip_error(void) { return g_last_hip_error; }
+
+size_t moe_workspace_bytes(int T, int H, int I, int E1, int K1, int block_m, int scale_mode) {
+  const size_t f = moe_ffn_workspace_bytes(T, H, I, E1, K1, block_m, scale_mode);
+  if (f == 0) return 0;
+  const size_t a = moe_align_workspace_bytes(T, K1, E1);
+  return f > a ? f : a;
+}
 
 int moe_route_topk_plus_shared(const float* logits, int T, int E, int K, float shared_weight,
                                int32_t* topk_ids, float* topk_w, void* stream) {
@@ -352,13 +361,23 @@ int moe_fused_ffn(const uint16_t* x, const uint8_t* w13, const float* s13, const
                          block_expert, num_padded, topk_w, workspace, ws_bytes, stream);
 }
 
+// Events recorded between the stages of one layer call (for measurement): events[0] before
+// the first launch, events[i] after stage i, and the stage's name in names[i - 1].
+struct StageMarks {
+  void* const* events;
+  int n_events;
+  const char** names;
+  int recorded;
+};
+
 static int layer_forward(const uint16_t* x, const LogitSrc& src, const void* logits, const uint8_t* w13, const float* s13,
                       const uint8_t* w2, const float* s2, int scale_mode, int T, int H, int I, int E,
                       int K, float shared_weight, int block_m, int32_t* topk_ids, float* topk_w,
                       int32_t* sorted_slot_ids, int32_t* block_expert, int32_t* expert_counts,
                       int32_t* expert_offsets, int32_t* num_padded, void* align_ws,
                       size_t align_ws_bytes, void* ffn_ws, size_t ffn_ws_bytes, uint16_t* out,
-                      void* stream, const std::function<int(LogitSrc*, hipStream_t)>& gate) {
+                      void* stream, const std::function<int(LogitSrc*, hipStream_t)>& gate,
+                      StageMarks* marks = nullptr) {
   // every check of the four calls, before anything is launched
   if (T < 0 || T > kMaxT || E < 1 || K < 0) return SRMOE_ERR_INVALID_ARG;
   if (E > 255 || K > E || K > 15) return SRMOE_ERR_UNSUPPORTED;
@@ -374,53 +393,84 @@ static int layer_forward(const uint16_t* x, const LogitSrc& src, const void* log
   const FfnLayout L = ffn_layout(T, H, I, E1, K1, block_m, scale_mode);
   if (ffn_ws_bytes < L.total) return SRMOE_ERR_WORKSPACE;
   char* ws = static_cast<char*>(ffn_ws);
+  {
+    // x_q is written before the align runs: an align workspace that overlaps the FFN workspace
+    // must keep its scratch inside the slot-row region in front of x_q (it always does when the
+    // two start at the same address: the align scratch is a few bytes per entry, a slot row H*2)
+    const char* a0 = static_cast<const char*>(align_ws);
+    const size_t need = moe_align_workspace_bytes(T, K1, E1);
+    if (a0 < ws + L.total && ws < a0 + need && (a0 < ws || a0 + need > ws + L.xq)) return SRMOE_ERR_WORKSPACE;
+  }
   const bool blk = scale_mode == SRMOE_SCALE_BLOCK128;
   hipStream_t sm = as_stream(stream);
+  // after a stage: record the next event (when asked to) and pass the status on
+  auto mark = [&](int status, const char* name) -> int {
+    if (status != SRMOE_OK || !marks || marks->recorded >= marks->n_events) return status;
+    if (marks->names && marks->recorded > 0) marks->names[marks->recorded - 1] = name;
+    const hipError_t e = hipEventRecord(static_cast<hipEvent_t>(marks->events[marks->recorded]), sm);
+    if (e != hipSuccess) return hip_status(e);
+    marks->recorded++;
+    return SRMOE_OK;
+  };
+  st = mark(SRMOE_OK, "");
+  if (st != SRMOE_OK) return st;
   LogitSrc lsrc = src;
   if (gate) {
-    st = gate(&lsrc, sm);
+    st = mark(gate(&lsrc, sm), "router_gate");
     if (st != SRMOE_OK) return st;
   }
-  st = hip_status(launch_layer_front(lsrc, T, E, K, shared_weight, topk_ids, topk_w, x, H, blk,
-                                     reinterpret_cast<uint8_t*>(ws + L.xq),
-                                     reinterpret_cast<float*>(ws + L.sx), sm));
+  st = mark(hip_status(launch_layer_front(lsrc, T, E, K, shared_weight, topk_ids, topk_w, x, H, blk,
+                                          reinterpret_cast<uint8_t*>(ws + L.xq),
+                                          reinterpret_cast<float*>(ws + L.sx), sm)),
+            "front");
   if (st != SRMOE_OK) return st;
   if (moe_ffn_experts_one_kernel(H, I, block_m) && expert_ffn_decode_align_supported(T, K1)) {
     // decode shapes: the expert kernel derives the align layout itself (every workgroup
     // from topk_ids) and writes the align outputs, so the layer is three launches
     const AlignOut al{topk_ids, expert_counts, expert_offsets, num_padded, E1};
-    st = hip_status(launch_expert_ffn_decode(
-        reinterpret_cast<const uint8_t*>(ws + L.xq), reinterpret_cast<const float*>(ws + L.sx), w13,
-        s13, w2, s2, blk, sorted_slot_ids, block_expert, num_padded, &al, topk_w,
-        reinterpret_cast<float*>(ws + L.a), reinterpret_cast<uint16_t*>(ws + L.slot_out), T, H, I,
-        E1, K1, sm));
+    st = mark(hip_status(launch_expert_ffn_decode(
+                  reinterpret_cast<const uint8_t*>(ws + L.xq), reinterpret_cast<const float*>(ws + L.sx), w13,
+                  s13, w2, s2, blk, sorted_slot_ids, block_expert, num_padded, &al, topk_w, nullptr,
+                  reinterpret_cast<uint16_t*>(ws + L.slot_out), T, H, I, E1, K1, sm)),
+              "experts");
     if (st != SRMOE_OK) return st;
-    return moe_combine(T, K1, H, ffn_ws, ffn_ws_bytes, out, stream);
+    return mark(moe_combine(topk_w, T, K1, H, ffn_ws, ffn_ws_bytes, out, stream), "combine");
   }
-  st = moe_align_by_expert(topk_ids, T, K1, E1, block_m, sorted_slot_ids, block_expert, expert_counts,
-                           expert_offsets, num_padded, align_ws, align_ws_bytes, stream);
+  st = mark(moe_align_by_expert(topk_ids, T, K1, E1, block_m, sorted_slot_ids, block_expert, expert_counts,
+                                expert_offsets, num_padded, align_ws, align_ws_bytes, stream),
+            "align");
   if (st != SRMOE_OK) return st;
   if (block_m == 128 && down_wide_supported(I)) {
     // prefill shapes: the shared expert's down GEMM and the combine are one launch (the
     // shared expert's segment is the last one; its rows add the token's routed slot rows,
     // left by the routed experts' down launch before it, and store out)
-    st = moe_ffn_gate_up(w13, s13, scale_mode, T, H, I, E1, K1, block_m, sorted_slot_ids, block_expert,
-                         num_padded, ffn_ws, ffn_ws_bytes, stream);
+    st = mark(moe_ffn_gate_up(w13, s13, scale_mode, T, H, I, E1, K1, block_m, sorted_slot_ids, block_expert,
+                              num_padded, ffn_ws, ffn_ws_bytes, stream),
+              "gate_up");
     if (st != SRMOE_OK) return st;
     const int P_max = (int)sorted_capacity(T, K1, E1, block_m);
-    st = hip_status(launch_quant_a(reinterpret_cast<const float*>(ws + L.a), P_max, I, blk, sorted_slot_ids,
-                                   topk_w, T * K1, num_padded, reinterpret_cast<uint8_t*>(ws + L.aq),
-                                   reinterpret_cast<float*>(ws + L.sa), reinterpret_cast<float*>(ws + L.rs), sm));
+    st = mark(hip_status(launch_quant_a(reinterpret_cast<const float*>(ws + L.a), P_max, I, blk, sorted_slot_ids,
+                                        topk_w, T * K1, num_padded, reinterpret_cast<uint8_t*>(ws + L.aq),
+                                        reinterpret_cast<float*>(ws + L.sa), reinterpret_cast<float*>(ws + L.rs),
+                                        sm)),
+              "quant_a");
     if (st != SRMOE_OK) return st;
-    return hip_status(launch_down_wide_combine(
-        reinterpret_cast<const uint8_t*>(ws + L.aq), reinterpret_cast<const float*>(ws + L.sa), w2, s2, blk,
-        sorted_slot_ids, block_expert, expert_offsets + E, reinterpret_cast<const float*>(ws + L.rs),
-        reinterpret_cast<uint16_t*>(ws + L.slot_out), out, T, H, I, E1, K1, sm));
+    for (int part = 1; part <= 2; ++part) {
+      st = mark(hip_status(launch_down_wide_combine(
+                    reinterpret_cast<const uint8_t*>(ws + L.aq), reinterpret_cast<const float*>(ws + L.sa), w2,
+                    s2, blk, sorted_slot_ids, block_expert, expert_offsets + E,
+                    reinterpret_cast<const float*>(ws + L.rs), reinterpret_cast<uint16_t*>(ws + L.slot_out), out,
+                    T, H, I, E1, K1, part, sm)),
+                part == 1 ? "down_routed" : "down_shared_combine");
+      if (st != SRMOE_OK) return st;
+    }
+    return SRMOE_OK;
   }
-  st = moe_ffn_experts(w13, s13, w2, s2, scale_mode, T, H, I, E1, K1, block_m, sorted_slot_ids,
-                       block_expert, num_padded, topk_w, ffn_ws, ffn_ws_bytes, stream);
+  st = mark(moe_ffn_experts(w13, s13, w2, s2, scale_mode, T, H, I, E1, K1, block_m, sorted_slot_ids,
+                            block_expert, num_padded, topk_w, ffn_ws, ffn_ws_bytes, stream),
+            moe_ffn_experts_one_kernel(H, I, block_m) ? "experts" : "gate_up+quant_a+down");
   if (st != SRMOE_OK) return st;
-  return moe_combine(T, K1, H, ffn_ws, ffn_ws_bytes, out, stream);
+  return mark(moe_combine(topk_w, T, K1, H, ffn_ws, ffn_ws_bytes, out, stream), "combine");
 }
 
 int moe_layer_forward(const uint16_t* x, const float* logits, const uint8_t* w13, const float* s13,
@@ -434,6 +484,26 @@ int moe_layer_forward(const uint16_t* x, const float* logits, const uint8_t* w13
                        shared_weight, block_m, topk_ids, topk_w, sorted_slot_ids, block_expert,
                        expert_counts, expert_offsets, num_padded, align_ws, align_ws_bytes, ffn_ws,
                        ffn_ws_bytes, out, stream, nullptr);
+}
+
+int moe_layer_forward_staged(const uint16_t* x, const float* logits, const uint8_t* w13, const float* s13,
+                             const uint8_t* w2, const float* s2, int scale_mode, int T, int H, int I, int E,
+                             int K, float shared_weight, int block_m, int32_t* topk_ids, float* topk_w,
+                             int32_t* sorted_slot_ids, int32_t* block_expert, int32_t* expert_counts,
+                             int32_t* expert_offsets, int32_t* num_padded, void* align_ws,
+                             size_t align_ws_bytes, void* ffn_ws, size_t ffn_ws_bytes, uint16_t* out,
+                             void* stream, void* const* events, int n_events, const char** stage_names,
+                             int* n_recorded) {
+  if (n_events < 0 || (n_events > 0 && !events)) return SRMOE_ERR_INVALID_ARG;
+  for (int i = 0; i < n_events; ++i)
+    if (!events[i]) return SRMOE_ERR_INVALID_ARG;
+  StageMarks marks{events, n_events, stage_names, 0};
+  const int st = layer_forward(x, LogitSrc{logits, nullptr, 0, 0}, logits, w13, s13, w2, s2, scale_mode, T, H, I,
+                               E, K, shared_weight, block_m, topk_ids, topk_w, sorted_slot_ids, block_expert,
+                               expert_counts, expert_offsets, num_padded, align_ws, align_ws_bytes, ffn_ws,
+                               ffn_ws_bytes, out, stream, nullptr, &marks);
+  if (n_recorded) *n_recorded = marks.recorded;
+  return st;
 }
 
 size_t moe_route_from_x_workspace_bytes(int T, int H, int E) {
@@ -504,12 +574,15 @@ int moe_layer_forward_from_x(const uint16_t* x, const float* w_router, const flo
                        });
 }
 
-int moe_combine(int T, int K1, int H, const void* workspace, size_t ws_bytes, uint16_t* out,
-                void* stream) {
+int moe_combine(const float* topk_w, int T, int K1, int H, const void* workspace, size_t ws_bytes,
+                uint16_t* out, void* stream) {
   if (T < 0 || T > kMaxT || K1 < 1 || H <= 0) return SRMOE_ERR_INVALID_ARG;
   if (K1 > 16 || H % 128 != 0 || (size_t)T * K1 * H >= ((size_t)1 << 31)) return SRMOE_ERR_UNSUPPORTED;
   if (T == 0) return SRMOE_OK;
   if (!workspace || !out || !aligned16(workspace) || !aligned16(out)) return SRMOE_ERR_INVALID_ARG;
+  // the slot rows already carry their routing weight (the down GEMM's epilogue applies it), so
+  // topk_w is not read here; it may be NULL
+  if (topk_w && !aligned16(topk_w)) return SRMOE_ERR_INVALID_ARG;
   if (ws_bytes < (size_t)T * K1 * H * 2) return SRMOE_ERR_WORKSPACE;
   return hip_status(launch_combine(static_cast<const uint16_t*>(workspace), nullptr, T, K1, H, out,
                                    as_stream(stream)));

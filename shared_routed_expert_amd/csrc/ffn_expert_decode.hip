@@ -14,7 +14,8 @@
 //  phase 2  g, u -> a = silu(g) * u -> FP8 a_q with the row (or row x 128-column
 //           group) absmax scale, in LDS; the row's output scale is its routing
 //           weight (times the FP8 scale per channel). a itself (float32) is also
-//           stored to the workspace, where the split kernels keep it.
+//           stored to the workspace, where the split kernels keep it, when a_out
+//           is given.
 //  phase 3  down: each wavefront takes every eighth group of 64 output columns;
 //           a group's 64 rows of w2[e] are 64 * I contiguous bytes, loaded as
 //           1 KB runs and passed through LDS into the swap-AB fragment layout
@@ -396,10 +397,13 @@ __global__ void __launch_bounds__(512) expert_ffn_decode_kernel(
       av[m] = valid ? silu(g) * u : 0.f;
       amax = fmaxf(amax, fabsf(av[m]));
     }
-    // the float32 product also goes to the workspace (sorted-row order), where the split path keeps it
-    float* arow = a_out + (size_t)(bb * 16 + r) * I + part * C;
+    // the float32 product also goes to the workspace (sorted-row order), where the split path
+    // keeps it, unless a_out is null (the whole-layer call, which never reads it back)
+    if (a_out) {
+      float* arow = a_out + (size_t)(bb * 16 + r) * I + part * C;
 #pragma unroll
-    for (int m = 0; m < C; m += 2) *reinterpret_cast<float2*>(arow + m) = make_float2(av[m], av[m + 1]);
+      for (int m = 0; m < C; m += 2) *reinterpret_cast<float2*>(arow + m) = make_float2(av[m], av[m + 1]);
+    }
     const float wgt = wgt_s[r];
     // per channel: the row's 32 threads; block: the 128 / C threads of a 128-column group
     const float scale = fp8_scale(group_max(amax, kBlock ? kGroup / C : 32));

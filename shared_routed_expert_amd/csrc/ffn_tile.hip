@@ -688,7 +688,8 @@ hipError_t launch_down_wide_combine(const uint8_t* aq, const float* sa, const ui
                                     bool block, const int32_t* sorted, const int32_t* block_expert,
                                     const int32_t* shared_first, const float* row_scale,
                                     uint16_t* slot_out, uint16_t* out, int T, int H, int I, int E1, int K1,
-                                    hipStream_t stream) {
+                                    int parts, hipStream_t stream) {
+  // parts: bit 0 the routed experts' launch, bit 1 the shared expert's launch with the combine
   if (!down_wide_supported(I)) return hipErrorInvalidValue;
   const int nb = (int)(sorted_capacity(T, K1, E1, kTBM) / kTBM);
   const int nbs = (T + kTBM - 1) / kTBM;
@@ -697,12 +698,14 @@ hipError_t launch_down_wide_combine(const uint8_t* aq, const float* sa, const ui
   const dim3 grid_c(nbs * ((H + 128 * kCombTiles - 1) / (128 * kCombTiles)));
 #define SRMOE_DOWN_COMB(B, KS)                                                                          \
   do {                                                                                                  \
-    hipLaunchKernelGGL((down_wide_kernel<B, KS, kDownTiles, kBlockedOut>), grid, blk, 0, stream, aq, sa, w2, \
-                       s2, sorted, block_expert, shared_first, row_scale, slot_out, T, H, I, K1, nullptr, \
-                       0);                                                                              \
-    hipLaunchKernelGGL((down_wide_kernel<B, KS, kCombTiles, kCombineOut>), grid_c, blk, 0, stream, aq, sa, w2, \
-                       s2, sorted, block_expert, shared_first, row_scale, slot_out, T, H, I, K1, out,  \
-                       nbs);                                                                            \
+    if (parts & 1)                                                                                      \
+      hipLaunchKernelGGL((down_wide_kernel<B, KS, kDownTiles, kBlockedOut>), grid, blk, 0, stream, aq, sa, \
+                         w2, s2, sorted, block_expert, shared_first, row_scale, slot_out, T, H, I, K1,   \
+                         nullptr, 0);                                                                   \
+    if (parts & 2)                                                                                      \
+      hipLaunchKernelGGL((down_wide_kernel<B, KS, kCombTiles, kCombineOut>), grid_c, blk, 0, stream, aq, sa, \
+                         w2, s2, sorted, block_expert, shared_first, row_scale, slot_out, T, H, I, K1, out, \
+                         nbs);                                                                          \
   } while (0)
   if (I <= kGroup) {
     if (block) SRMOE_DOWN_COMB(true, 1); else SRMOE_DOWN_COMB(false, 1);

@@ -105,7 +105,7 @@ class FusedMoE:
             between("down")
 
     def combine(self, stream=None):
-        L.moe_combine(self.T, self.K1, self.H, self.ws, self.ws_bytes, self.out, stream)
+        L.moe_combine(self.topk_w, self.T, self.K1, self.H, self.ws, self.ws_bytes, self.out, stream)
 
     def forward(self, x, logits, W: DeviceWeights, shared_weight=1.0, stream=None):
         self.route(logits, shared_weight, stream)
@@ -122,6 +122,16 @@ class FusedMoE:
                             self.block_expert, self.expert_counts, self.expert_offsets, self.num_padded,
                             self.align_ws, self.align_ws_bytes, self.ws, self.ws_bytes, self.out, stream)
         return self.out
+
+    def forward_staged(self, x, logits, W: DeviceWeights, shared_weight=1.0, events=(), stream=None):
+        """moe_layer_forward_staged: the same layer with `events` (torch.cuda.Event, already
+        created) recorded between its stages; returns the stage names."""
+        T, H, I, E1, K1, bm = self.dims()
+        return L.moe_layer_forward_staged(x, logits, W.w13, W.s13, W.w2, W.s2, self.scale_mode, T, H, I, self.E,
+                                          self.K, shared_weight, bm, self.topk_ids, self.topk_w,
+                                          self.sorted_slot_ids, self.block_expert, self.expert_counts,
+                                          self.expert_offsets, self.num_padded, self.align_ws, self.align_ws_bytes,
+                                          self.ws, self.ws_bytes, self.out, list(events), stream)
 
     def forward_from_x(self, x, w_router, bias, W: DeviceWeights, shared_weight=1.0, stream=None):
         """The layer from x and the router weight (moe_layer_forward_from_x: the router gate

@@ -56,6 +56,22 @@ def run_layer(inp, block_m, shared_weight=1.0, layer=None, W=None):
     return layer, W
 
 
+_GEN_CACHE = []   # (config, inputs), the most recently used last; at most two kept
+
+
+def generate_cached(cfg):
+    """generate(cfg), keeping the last two full-size input sets (the unsharded block-scale
+    set takes about a minute to synthesise and is used by two tests)."""
+    for i, (c, inp) in enumerate(_GEN_CACHE):
+        if c == cfg:
+            _GEN_CACHE.append(_GEN_CACHE.pop(i))
+            return inp
+    inp = generate(cfg)
+    _GEN_CACHE.append((cfg, inp))
+    del _GEN_CACHE[:-2]
+    return inp
+
+
 def small_cfg(name, T, H, I, E, K, mode="channel", seed=0, zipf=None):
     return MoEConfig(name, T=T, H=H, E=E, K=K, I=I, scale_mode=mode, seed=seed, zipf_s=zipf)
 
@@ -65,7 +81,7 @@ def x_f32(inp):
 
 
 __all__ = ["DEV", "TOL", "note", "to_dev", "bf16_dev", "bf16_to_np", "token_rel_err", "make_layer",
-           "run_layer", "small_cfg", "x_f32", "generate"]
+           "run_layer", "small_cfg", "x_f32", "generate", "generate_cached"]
 
 
 # ---------------------------------------------------------------------------- FP8 tie allowance

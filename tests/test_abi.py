@@ -222,13 +222,64 @@ def test_combine_unfused_rejects(L):
 
 def test_combine_rejects(L):
     f = lambda *a: L.moe_combine(*a, stream=0, check=False)
-    assert f(-1, 9, 5120, FAKE, 1 << 30, FAKE) == -1
-    assert f(64, 0, 5120, FAKE, 1 << 30, FAKE) == -1
-    assert f(64, 9, 5000, FAKE, 1 << 30, FAKE) == -2
-    assert f(64, 9, 5120, None, 1 << 30, FAKE) == -1
-    assert f(64, 9, 5120, FAKE, 1 << 30, MIS) == -1
-    assert f(64, 9, 5120, FAKE, 64 * 9 * 5120 * 2 - 1, FAKE) == -3
-    assert f(0, 9, 5120, None, 0, None) == 0
+    assert f(FAKE, -1, 9, 5120, FAKE, 1 << 30, FAKE) == -1
+    assert f(FAKE, 64, 0, 5120, FAKE, 1 << 30, FAKE) == -1
+    assert f(FAKE, 64, 9, 5000, FAKE, 1 << 30, FAKE) == -2
+    assert f(FAKE, 64, 9, 5120, None, 1 << 30, FAKE) == -1
+    assert f(FAKE, 64, 9, 5120, FAKE, 1 << 30, MIS) == -1
+    assert f(MIS, 64, 9, 5120, FAKE, 1 << 30, FAKE) == -1        # topk_w misaligned
+    assert f(FAKE, 64, 9, 5120, FAKE, 64 * 9 * 5120 * 2 - 1, FAKE) == -3
+    assert f(None, 64, 9, 5120, FAKE, 64 * 9 * 5120 * 2 - 1, FAKE) == -3   # topk_w may be NULL
+    assert f(None, 0, 9, 5120, None, 0, None) == 0
+
+
+def test_combine_signature_takes_topk_w(L):
+    """moe_combine(topk_w, T, K1, H, workspace, ws_bytes, out, stream): the routing weights
+    come first, as the boundary's contract lists them."""
+    import ctypes
+    hdr = open(HEADER).read()
+    assert re.search(r"int moe_combine\(const float\* topk_w, int T, int K1, int H, const void\* workspace,"
+                     r"\s+size_t ws_bytes,\s+uint16_t\* out, void\* stream\);", hdr)
+    assert L.lib.moe_combine.argtypes[0] is ctypes.c_void_p and len(L.lib.moe_combine.argtypes) == 8
+
+
+def test_one_workspace_size_for_align_ffn_and_combine(L):
+    """moe_workspace_bytes covers both the align and the FFN workspace for every shape, and is
+    0 exactly where the FFN shape is unsupported."""
+    shapes = [(64, 5120, 192, 161, 9, 16, 0), (4096, 5120, 192, 161, 9, 128, 0), (16384, 5120, 192, 161, 9, 128, 0),
+              (4096, 5120, 1536, 161, 9, 128, 1), (16, 128, 32, 9, 3, 16, 0), (0, 256, 64, 9, 3, 32, 0),
+              (20000, 256, 64, 256, 16, 64, 0)]
+    for T, H, I, E1, K1, bm, mode in shapes:
+        n = L.moe_workspace_bytes(T, H, I, E1, K1, bm, mode)
+        assert n >= L.moe_ffn_workspace_bytes(T, H, I, E1, K1, bm, mode) > 0
+        assert n >= L.moe_align_workspace_bytes(T, K1, E1)
+        assert n == max(L.moe_ffn_workspace_bytes(T, H, I, E1, K1, bm, mode), L.moe_align_workspace_bytes(T, K1, E1))
+    assert L.moe_workspace_bytes(64, 5000, 192, 161, 9, 16, 0) == 0     # H % 128
+    assert L.moe_workspace_bytes(64, 5120, 192, 161, 9, 16, 1) == 0     # block mode needs I % 128 == 0
+    assert L.moe_workspace_bytes(64, 5120, 192, 161, 9, 48, 0) == 0     # block_m
+
+
+def test_moe_status_string_matches(L):
+    for st in (0, -1, -2, -3, -4, 7):
+        assert L.moe_status_string(st) == L.lib.srmoe_status_string(st).decode()
+    assert L.moe_status_string(-3) == "workspace too small"
+
+
+def test_layer_forward_staged_rejects(L):
+    """The measurement form runs the layer's checks (nothing is launched) and checks its event list."""
+    import ctypes
+    base = [FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, 64, 5120, 192, 160, 8, 1.0, 16] + [FAKE] * 7 + \
+           [FAKE, 1 << 30, FAKE, 1 << 40, FAKE, 0]
+    ev = (ctypes.c_void_p * 2)(FAKE, FAKE)
+    nul = (ctypes.c_void_p * 2)(FAKE, None)
+    f = lambda args, events, n: L.lib.moe_layer_forward_staged(*args, events, n, None, None)
+    assert f(base, ev, -1) == -1
+    assert f(base, None, 2) == -1
+    assert f(base, nul, 2) == -1
+    bad = list(base); bad[7] = -1
+    assert f(bad, ev, 2) == -1
+    bad = list(base); bad[8] = 1000
+    assert f(bad, ev, 2) == -2
 
 
 def test_no_cpu_fallback_in_product(L):

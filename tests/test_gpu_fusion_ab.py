@@ -12,7 +12,7 @@ import pytest
 import torch
 
 import oracle
-from tests.gpu_util import note, to_dev, bf16_dev, make_layer, small_cfg
+from tests.gpu_util import note, to_dev, bf16_dev, bf16_to_np, make_layer, small_cfg, x_f32, check_rows_with_ties
 from workloads import CONFIGS, generate
 
 pytestmark = pytest.mark.gpu
@@ -46,6 +46,29 @@ def test_unfused_equals_fused(cfg, bm):
     assert torch.equal(unf.out.view(torch.int16), fused.out.view(torch.int16))
     assert torch.equal(unf.routed.topk_ids, fused.topk_ids[:, :cfg.K])
     assert torch.equal(unf.routed.topk_w.view(torch.int32), fused.topk_w[:, :cfg.K].contiguous().view(torch.int32))
+
+
+@pytest.mark.parametrize("cfg,bm", CASES, ids=[f"{c.name}-{bm}" for c, bm in CASES])
+def test_unfused_against_oracle(cfg, bm):
+    """The unfused GPU layer (routed top-K pass + separate shared pass + add) against the
+    oracle's unfused form, the pages' "traditional" formulation (intelliparadigm, section
+    2.1): every token within 2e-2 (inf-norm relative), with the FP8 tie allowance."""
+    inp = generate(cfg)
+    c = inp.cfg
+    note(f"unfused vs oracle {cfg.name} bm={bm}")
+    x, lg = bf16_dev(inp.x_bf16), to_dev(inp.logits)
+    _, W = make_layer(inp, bm)
+    unf = _unfused(inp, bm, W)
+    unf.forward(x, lg, W, 1.0)
+    torch.cuda.synchronize()
+    ids_r, _ = oracle.route_topk(inp.logits, c.K)
+    assert np.array_equal(unf.routed.topk_ids.cpu().numpy(), ids_r)
+    ref = oracle.moe_unfused(x_f32(inp), inp.logits, c.K, inp.w13_q, inp.s13, inp.w2_q, inp.s2)
+    got = bf16_to_np(unf.out)
+    # the tie allowance walks the token's slots: the routed ones and the shared expert (weight 1)
+    ids9, w9 = oracle.route_topk_plus_shared(inp.logits, c.K)
+    e, n_tie = check_rows_with_ties(got, ref, inp, [[(t, k) for k in range(c.K1)] for t in range(c.T)], ids9, w9)
+    note(f"  unfused {cfg.name}: max per-token rel err {e:.3e}, tokens on the tie allowance {n_tie}")
 
 
 def test_unfused_split_shared_pass_within_tolerance():

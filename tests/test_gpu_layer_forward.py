@@ -76,3 +76,67 @@ def test_layer_forward_matches_four_calls(cfg, bm):
     got = _outputs(b)
     for k in ref:
         assert np.array_equal(ref[k], got[k]), k
+
+
+@pytest.mark.parametrize("name,bm,stages", [
+    ("decode", 16, ["front", "experts", "combine"]),
+    ("prefill", 128, ["front", "align", "gate_up", "quant_a", "down_routed", "down_shared_combine"]),
+])
+def test_layer_forward_staged_matches(name, bm, stages):
+    """The measurement form records one event per stage and computes the same bits."""
+    from shared_routed_expert_amd import _lib as L
+    inp = generate(CONFIGS[name])
+    note(f"layer_forward_staged {name} bm={bm}")
+    x, lg = bf16_dev(inp.x_bf16), to_dev(inp.logits)
+    a, W = make_layer(inp, bm)
+    a.forward_fused(x, lg, W, 1.0)
+    torch.cuda.synchronize()
+    ref = _outputs(a)
+    b, _ = make_layer(inp, bm)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(8)]
+    for e in evs:
+        e.record()   # creates the underlying events
+    torch.cuda.synchronize()
+    names = b.forward_staged(x, lg, W, 1.0, evs)
+    torch.cuda.synchronize()
+    assert names == stages
+    got = _outputs(b)
+    for k in ref:
+        assert np.array_equal(ref[k], got[k]), k
+    ms = [evs[i].elapsed_time(evs[i + 1]) for i in range(len(names))]
+    assert all(m >= 0 for m in ms)
+
+
+@pytest.mark.parametrize("cfg,bm", [(CONFIGS["decode"], 16), (CONFIGS["prefill"], 128),
+                                    (small_cfg("ragged", T=77, H=384, I=96, E=12, K=3, seed=11), 32)])
+def test_one_workspace_serves_align_and_ffn(cfg, bm):
+    """One buffer of moe_workspace_bytes passed as both the align and the FFN workspace (the
+    four calls and moe_layer_forward) gives the same bits as separate buffers; moe_combine
+    gives the same bits with topk_w NULL or given."""
+    from shared_routed_expert_amd import _lib as L
+    inp = generate(cfg)
+    c = inp.cfg
+    note(f"one workspace {cfg.name} bm={bm}")
+    x, lg = bf16_dev(inp.x_bf16), to_dev(inp.logits)
+    a, W = make_layer(inp, bm)
+    a.forward(x, lg, W, 1.0)
+    torch.cuda.synchronize()
+    ref = a.out.view(torch.int16).clone()
+    n = L.moe_workspace_bytes(c.T, c.H, c.I, c.E1, c.K1, bm, W.scale_mode)
+    assert n >= max(a.ws_bytes, a.align_ws_bytes)
+    b, _ = make_layer(inp, bm)
+    one = torch.empty(n, dtype=torch.uint8, device=DEV)
+    b.ws, b.ws_bytes, b.align_ws, b.align_ws_bytes = one, n, one, n
+    b.forward(x, lg, W, 1.0)
+    torch.cuda.synchronize()
+    assert torch.equal(b.out.view(torch.int16), ref)
+    b.out.zero_()
+    b.forward_fused(x, lg, W, 1.0)
+    torch.cuda.synchronize()
+    assert torch.equal(b.out.view(torch.int16), ref)
+    # the combine alone, on the slot rows the four calls left: topk_w given or NULL
+    b.forward(x, lg, W, 1.0)
+    b.out.zero_()
+    L.moe_combine(None, c.T, c.K1, c.H, b.ws, b.ws_bytes, b.out)
+    torch.cuda.synchronize()
+    assert torch.equal(b.out.view(torch.int16), ref)
