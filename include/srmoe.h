@@ -281,6 +281,29 @@ int moe_layer_forward_staged(const uint16_t* x, const float* logits, const uint8
                              int* n_recorded);
 
 /* ---------------------------------------------------------------------------
+ * For callers that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): moe_layer_forward with every
+ * intermediate -- routing tables, sort arrays, align and FFN workspaces -- in a device
+ * array inside the library instead of caller buffers. The caller passes the inputs and
+ * `out` only; arguments and result are those of moe_layer_forward (same kernels, same
+ * bits). The call allocates nothing: no hipMalloc, hipFree or allocating library routine.
+ *   - The array holds SRMOE_NOALLOC_SCRATCH_BYTES (64 MiB) on each device it runs on, from
+ *     the first call on that device until the process ends.
+ *   - Sizes whose intermediates need more than that return SRMOE_ERR_WORKSPACE before
+ *     anything is launched: the carve is the routing tables, the sort arrays, the align
+ *     workspace and moe_ffn_workspace_bytes(...), each rounded up to 256 bytes (at H =
+ *     5120, I = 192, 161 experts and 9 slots: up to 609 tokens with 16-row blocks, 444
+ *     with 128-row blocks).
+ *   - Every call on a device shares that device's array and leaves the last call's
+ *     contents there: calls that overlap in time on one device (other streams, other host
+ *     threads) race. Nothing in the array needs to start at zero.
+ * ------------------------------------------------------------------------- */
+#define SRMOE_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int moe_layer_forward_noalloc(const uint16_t* x, const float* logits, const uint8_t* w13, const float* s13,
+                              const uint8_t* w2, const float* s2, int scale_mode, int T, int H, int I, int E,
+                              int K, float shared_weight, int block_m, uint16_t* out, void* stream);
+
+/* ---------------------------------------------------------------------------
  * Attention side of the same model: the per-head QK norm fused with the rotary
  * position embedding (intelliparadigm section 2.2; Optimizing GLM4-MoE for
  * production section 2: both are per-head steps, so one kernel does both; GLM4-MoE

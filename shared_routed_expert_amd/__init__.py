@@ -13,7 +13,8 @@ _BINDING = ("lib", "LIB_PATH", "SrmoeError", "SCALE_PER_CHANNEL", "SCALE_BLOCK12
             "moe_route_topk", "moe_combine_unfused", "moe_router_logits", "moe_router_workspace_bytes",
             "moe_ffn_workspace_bytes", "moe_ffn_workspace_offsets", "moe_qk_norm_rope", "moe_rope_cos_sin_table",
             "moe_route_from_x", "moe_route_from_x_workspace_bytes", "moe_layer_forward_from_x",
-            "moe_workspace_bytes", "moe_status_string", "moe_layer_forward_staged")
+            "moe_workspace_bytes", "moe_status_string", "moe_layer_forward_staged",
+            "moe_layer_forward_noalloc", "NOALLOC_SCRATCH_BYTES")
 _LAYER = ("FusedMoE", "UnfusedMoE", "DeviceWeights")
 
 

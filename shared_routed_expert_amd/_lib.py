@@ -49,6 +49,7 @@ def _load():
         "moe_layer_forward_staged": ([P, P, P, P, P, P, I, I, I, I, I, I, F, I, P, P, P, P, P, P, P, P, Z, P, Z, P,
                                       P, P, I, P, P], I),
         "moe_workspace_bytes": ([I, I, I, I, I, I, I], Z),
+        "moe_layer_forward_noalloc": ([P, P, P, P, P, P, I, I, I, I, I, I, F, I, P, P], I),
         "moe_status_string": ([I], ctypes.c_char_p),
         "moe_qk_norm_rope": ([P, I, I, I, I, I, I, P, P, F, P, P, I, I, P], I),
         "moe_route_from_x": ([P, P, P, I, I, I, I, F, P, P, P, Z, P], I),
@@ -79,7 +80,7 @@ EXPORTED = ("moe_route_topk_plus_shared", "moe_align_by_expert", "moe_fused_ffn"
             "moe_route_from_x_workspace_bytes", "moe_layer_forward_from_x", "moe_sorted_capacity",
             "moe_align_workspace_bytes", "moe_ffn_workspace_bytes", "moe_ffn_workspace_offsets",
             "srmoe_status_string", "srmoe_last_hip_error", "moe_workspace_bytes", "moe_status_string",
-            "moe_layer_forward_staged")
+            "moe_layer_forward_staged", "moe_layer_forward_noalloc")
 
 
 def _ptr(t):
@@ -249,6 +250,16 @@ def moe_layer_forward_staged(x, logits, w13, s13, w2, s2, scale_mode, T, H, I, E
     if check:
         _check("moe_layer_forward_staged", st)
     return [names[i].decode() for i in range(max(rec.value - 1, 0))]
+
+
+def moe_layer_forward_noalloc(x, logits, w13, s13, w2, s2, scale_mode, T, H, I, E, K, shared_weight, block_m, out,
+                              stream=None, check=True):
+    st = lib.moe_layer_forward_noalloc(_ptr(x), _ptr(logits), _ptr(w13), _ptr(s13), _ptr(w2), _ptr(s2), scale_mode,
+                                       T, H, I, E, K, shared_weight, block_m, _ptr(out), _stream(stream))
+    return _check("moe_layer_forward_noalloc", st) if check else st
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20   # SRMOE_NOALLOC_SCRATCH_BYTES
 
 
 def moe_qk_norm_rope(qkv, T, num_q_heads, num_kv_heads, head_dim, rotary_dim, neox, q_norm_w, k_norm_w, eps,

@@ -3,6 +3,7 @@
 #include "srmoe.h"
 
 #include <functional>
+#include <mutex>
 
 #include "front_dev.hpp"
 
@@ -56,11 +57,17 @@ hipError_t launch_rope_table(float*, int, int, double, hipStream_t);
 
 using namespace srmoe;
 
+// The array behind moe_layer_forward_noalloc (one copy per device; see there). In host code
+// this name is only a handle for hipGetSymbolAddress, never a device address.
+static __device__ __align__(256) uint8_t scratch[SRMOE_NOALLOC_SCRATCH_BYTES];
+
+
 namespace {
 
 thread_local int g_last_hip_error = 0;
 
 constexpr int kMaxT = 1 << 20;
+constexpr int kMaxNoAllocDevices = 64;
 
 inline size_t al256(size_t n) { return (n + 255) / 256 * 256; }
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -504,6 +511,83 @@ int moe_layer_forward_staged(const uint16_t* x, const float* logits, const uint8
                                ffn_ws_bytes, out, stream, nullptr, &marks);
   if (n_recorded) *n_recorded = marks.recorded;
   return st;
+}
+
+// ---------------------------------------------------------------------------------------
+// moe_layer_forward_noalloc: the layer with every intermediate (routing tables, sort arrays,
+// align and FFN workspaces) in the library's own device array, for callers that cannot
+// allocate. Each device that runs it holds its own copy of the array until the process ends;
+// its device address is looked up once per device (hipGetSymbolAddress) and only that
+// address is handed to the kernels. Calls on one device share the array: calls that overlap
+// in time on one device race.
+static std::mutex g_noalloc_mu;
+static void* g_noalloc_ptr[kMaxNoAllocDevices];
+
+static int noalloc_scratch(void** ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e);
+  if (dev < 0 || dev >= kMaxNoAllocDevices) return SRMOE_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_noalloc_mu);
+  if (!g_noalloc_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_status(e);
+    if (!p) return SRMOE_ERR_HIP;
+    g_noalloc_ptr[dev] = p;
+  }
+  *ptr = g_noalloc_ptr[dev];
+  return SRMOE_OK;
+}
+
+// Carve of the array for one call (each piece 256-byte aligned); 0 when the shape is invalid.
+struct NoAllocLayout {
+  size_t ids, w, sorted, bexp, counts, offsets, npad, align_ws, ffn_ws, align_bytes, ffn_bytes, total;
+};
+static NoAllocLayout noalloc_layout(int T, int H, int I, int E, int K, int block_m, int scale_mode) {
+  NoAllocLayout L{};
+  const int E1 = E + 1, K1 = K + 1;
+  const size_t P = sorted_capacity(T, K1, E1, block_m);
+  size_t off = 0;
+  L.ids = off;      off += al256((size_t)T * K1 * 4);
+  L.w = off;        off += al256((size_t)T * K1 * 4);
+  L.sorted = off;   off += al256(P * 4);
+  L.bexp = off;     off += al256(P / block_m * 4);
+  L.counts = off;   off += al256((size_t)E1 * 4);
+  L.offsets = off;  off += al256((size_t)(E1 + 1) * 4);
+  L.npad = off;     off += 256;
+  L.align_bytes = moe_align_workspace_bytes(T, K1, E1);
+  L.align_ws = off; off += al256(L.align_bytes);
+  L.ffn_bytes = moe_ffn_workspace_bytes(T, H, I, E1, K1, block_m, scale_mode);
+  L.ffn_ws = off;   off += al256(L.ffn_bytes);
+  L.total = off;
+  return L;
+}
+
+int moe_layer_forward_noalloc(const uint16_t* x, const float* logits, const uint8_t* w13, const float* s13,
+                              const uint8_t* w2, const float* s2, int scale_mode, int T, int H, int I, int E,
+                              int K, float shared_weight, int block_m, uint16_t* out, void* stream) {
+  // the shape checks of moe_layer_forward first (nothing of the array is touched before them)
+  if (T < 0 || T > kMaxT || E < 1 || K < 0) return SRMOE_ERR_INVALID_ARG;
+  if (E > 255 || K > E || K > 15) return SRMOE_ERR_UNSUPPORTED;
+  int st = check_ffn_dims(scale_mode, T, H, I, E + 1, K + 1, block_m);
+  if (st != SRMOE_OK) return st;
+  if (T == 0) return SRMOE_OK;
+  const NoAllocLayout L = noalloc_layout(T, H, I, E, K, block_m, scale_mode);
+  if (L.ffn_bytes == 0 || L.total > (size_t)SRMOE_NOALLOC_SCRATCH_BYTES) return SRMOE_ERR_WORKSPACE;
+  const void* ptrs[] = {x, logits, w13, s13, w2, s2, out};
+  for (const void* p : ptrs)
+    if (!p || !aligned16(p)) return SRMOE_ERR_INVALID_ARG;
+  void* base = nullptr;
+  st = noalloc_scratch(&base);
+  if (st != SRMOE_OK) return st;
+  char* sb = static_cast<char*>(base);
+  return layer_forward(x, LogitSrc{logits, nullptr, 0, 0}, logits, w13, s13, w2, s2, scale_mode, T, H, I, E, K,
+                       shared_weight, block_m, reinterpret_cast<int32_t*>(sb + L.ids),
+                       reinterpret_cast<float*>(sb + L.w), reinterpret_cast<int32_t*>(sb + L.sorted),
+                       reinterpret_cast<int32_t*>(sb + L.bexp), reinterpret_cast<int32_t*>(sb + L.counts),
+                       reinterpret_cast<int32_t*>(sb + L.offsets), reinterpret_cast<int32_t*>(sb + L.npad),
+                       sb + L.align_ws, L.align_bytes, sb + L.ffn_ws, L.ffn_bytes, out, stream, nullptr);
 }
 
 size_t moe_route_from_x_workspace_bytes(int T, int H, int E) {

@@ -374,3 +374,14 @@ def test_layer_forward_from_x_rejects(L):
         assert f(**{name: None}) == -1, name
     assert f(router_ws_bytes=rwb - 1) == -3 and f(ffn_ws_bytes=fwb - 1) == -3 and f(align_ws_bytes=awb - 1) == -3
     assert f(T=0, x=None, out=None) == 0
+
+
+def test_noalloc_rejects_sizes_beyond_the_array(L):
+    """Host-side checks of moe_layer_forward_noalloc: nothing is launched and the array is
+    never looked up for these."""
+    args = [FAKE] * 6
+    # 4,096 prefill tokens need ~450 MB of intermediates: refused before any launch
+    assert L.lib.moe_layer_forward_noalloc(*args, 0, 4096, 5120, 192, 160, 8, 1.0, 128, FAKE, None) == -3
+    assert L.lib.moe_layer_forward_noalloc(*args, 0, 64, 5120, 192, 160, 8, 1.0, 48, FAKE, None) == -2
+    assert L.lib.moe_layer_forward_noalloc(*args, 0, 64, 5120, 192, 160, 8, 1.0, 16, 0x10004, None) == -1
+    assert L.lib.moe_layer_forward_noalloc(*args, 0, 0, 5120, 192, 160, 8, 1.0, 16, None, None) == 0
