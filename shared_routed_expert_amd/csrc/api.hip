@@ -61,7 +61,6 @@ using namespace srmoe;
 // this name is only a handle for hipGetSymbolAddress, never a device address.
 static __device__ __align__(256) uint8_t scratch[SRMOE_NOALLOC_SCRATCH_BYTES];
 
-
 namespace {
 
 thread_local int g_last_hip_error = 0;
@@ -447,21 +446,33 @@ static int layer_forward(const uint16_t* x, const LogitSrc& src, const void* log
                                 expert_offsets, num_padded, align_ws, align_ws_bytes, stream),
             "align");
   if (st != SRMOE_OK) return st;
-  if (block_m == 128 && down_wide_supported(I)) {
-    // prefill shapes: the shared expert's down GEMM and the combine are one launch (the
-    // shared expert's segment is the last one; its rows add the token's routed slot rows,
-    // left by the routed experts' down launch before it, and store out)
+  if (block_m == 128) {
+    // prefill shapes: gate/up, the FP8 quantisation of a, then the down GEMM
+    const int P_max = (int)sorted_capacity(T, K1, E1, block_m);
     st = mark(moe_ffn_gate_up(w13, s13, scale_mode, T, H, I, E1, K1, block_m, sorted_slot_ids, block_expert,
                               num_padded, ffn_ws, ffn_ws_bytes, stream),
               "gate_up");
     if (st != SRMOE_OK) return st;
-    const int P_max = (int)sorted_capacity(T, K1, E1, block_m);
     st = mark(hip_status(launch_quant_a(reinterpret_cast<const float*>(ws + L.a), P_max, I, blk, sorted_slot_ids,
                                         topk_w, T * K1, num_padded, reinterpret_cast<uint8_t*>(ws + L.aq),
                                         reinterpret_cast<float*>(ws + L.sa), reinterpret_cast<float*>(ws + L.rs),
                                         sm)),
               "quant_a");
     if (st != SRMOE_OK) return st;
+    if (!down_wide_supported(I)) {
+      // I > 256: the K-looped down GEMM, then the combine
+      st = mark(hip_status(launch_down(reinterpret_cast<const uint8_t*>(ws + L.aq),
+                                       reinterpret_cast<const float*>(ws + L.sa), w2, s2, blk, sorted_slot_ids,
+                                       block_expert, num_padded, reinterpret_cast<const float*>(ws + L.rs),
+                                       reinterpret_cast<uint16_t*>(ws + L.slot_out), T, H, I, E1, K1, block_m,
+                                       sm)),
+                "down");
+      if (st != SRMOE_OK) return st;
+      return mark(moe_combine(topk_w, T, K1, H, ffn_ws, ffn_ws_bytes, out, stream), "combine");
+    }
+    // the shared expert's down GEMM and the combine are one launch (the shared expert's
+    // segment is the last one; its rows add the token's routed slot rows, left by the
+    // routed experts' down launch before it, and store out)
     for (int part = 1; part <= 2; ++part) {
       st = mark(hip_status(launch_down_wide_combine(
                     reinterpret_cast<const uint8_t*>(ws + L.aq), reinterpret_cast<const float*>(ws + L.sa), w2,

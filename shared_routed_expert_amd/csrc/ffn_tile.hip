@@ -380,27 +380,37 @@ __global__ void __launch_bounds__(256, 2) down_tile_kernel(
   }
 }
 
-// down for I <= 256 (at most two 128-byte K steps): no K loop. The workgroup
-// stages its block's 128 a_q rows (zero-filled from I to the K-step boundary)
-// and the w2 scales of its columns in LDS once; each wavefront then sweeps
-// kDownTiles 64-column tiles of w2[e] for one 64-row half, with the weights as
-// the MFMA A operand and two tiles' weight fragments in registers (a tile's set is
-// refilled two tiles ahead as soon as its MFMAs have consumed it). Inside a tile, row r of MFMA
-// tile n holds column (r / 4) * 16 + 4 * n + r % 4, so each lane ends with 16
-// consecutive output columns of a row. The bf16 tile then goes through a
-// wavefront-private LDS buffer so that 8 lanes write each row's 128 contiguous
-// bytes with one non-temporal store: slot_out is written once and read once by
-// the combine, and whole-line streaming stores keep it from evicting the w2
-// slices that the block's neighbours re-read from L2 (mixed with partial-line
-// stores the same reads and writes took about 1.7x as long). Workgroup = 2 row
-// halves x 2 interleaved column streams over 128 * kDownTiles columns; tiles
-// are ordered row block major and walked per XCD.
+// down for I <= 256 with 32x32x64 MFMAs: K = I in ceil(I / 64) steps of 64 bytes (three
+// exact steps at I = 192; a partial last step is zero-filled). Workgroup = 2 row halves x
+// 2 column streams; stream wc takes the 64-column tiles g * 2 NTL + wc + 2 j of w2[e]
+// (j < NTL), in 128 * NTL columns per workgroup, tiles ordered row block major and walked
+// per XCD.
+//  - Each wavefront holds its 64 a_q rows as the MFMA B operand for the whole launch,
+//    loaded once (lane l: row l % 32 of a 32-row tile, K bytes 32 (l / 32) of each step).
+//  - A tile's 64 rows of w2[e] are 64 * I contiguous bytes: the stream's two wavefronts load
+//    half each as 1 KB runs (16 bytes per lane: whole lines per instruction), a tile ahead,
+//    and store them to the stream's LDS buffer (rows padded by 16 bytes); the weight
+//    fragments (the A operand) are read from there. Weight row rho of a 32-row MFMA tile is
+//    output column 16 ((rho / 4) % 2) + 4 (rho / 8) + rho % 4, so that lane l ends with the 16
+//    consecutive columns 16 (l / 32) .. + 15 of token l % 32.
+//  - The bf16 results go through a wavefront-private LDS buffer so that 8 lanes write each
+//    row's 128 contiguous bytes with one non-temporal store: slot_out is written once and
+//    read once by the combine, and whole-line streaming stores keep it from evicting the
+//    w2 tiles that the block's neighbours re-read from L2.
 constexpr int kDownTiles = 4;
 constexpr int kCombTiles = 1;              // 64-column tiles per wavefront in the combining launch
-constexpr int kDownLD = 2 * kGroup + 16;   // LDS row stride of the a_q tile (bytes)
 constexpr int kStageLD = 128 + 16;         // LDS row stride of an output staging buffer
 
 typedef unsigned int u32x4_nt __attribute__((ext_vector_type(4)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+
+// D(32x32,f32) += A(32x64,fp8 e4m3) * B(64x32,fp8 e4m3): lane l supplies row/column l % 32
+// and the 32 K bytes at 32 (l / 32) of the 64-byte K step (A and B share the K mapping);
+// element v of lane l is D[8 (v / 4) + 4 (l / 32) + v % 4][l % 32]. Format 0 = OCP E4M3 for
+// both operands, E8M0 block scales fixed at 127 (= 1).
+__device__ __forceinline__ v16f mfma_32x32x64_fp8(const v8i& a, const v8i& b, const v16f& c) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
 
 // acc[c] += the c-th of the 8 bf16 values in v (low half of each word first)
 __device__ __forceinline__ void add_bf16x8(float (&acc)[8], const uint4& v) {
@@ -424,17 +434,20 @@ __device__ __forceinline__ void add_bf16x8(float (&acc)[8], const uint4& v) {
 // In the blocked layout the combining launch reads, per 128-token block and column block,
 // one contiguous run of 128 * K1 pieces of 256 bytes (the row layout scatters them).
 constexpr int kRowsOut = 0, kBlockedOut = 1, kCombineOut = 2;
-template <bool kBlock, int KS, int NTL, int kOut>
+template <bool kBlock, int KT, int NTL, int kOut>
 __global__ void __launch_bounds__(256, 2) down_wide_kernel(
     const uint8_t* __restrict__ aq, const float* __restrict__ sa, const uint8_t* __restrict__ w2,
     const float* __restrict__ s2, const int32_t* __restrict__ sorted,
     const int32_t* __restrict__ block_expert, const int32_t* __restrict__ rows,
     const float* __restrict__ row_scale, uint16_t* __restrict__ slot_out, int T, int H, int I,
     int K1, uint16_t* __restrict__ out, int comb_blocks) {
-  constexpr int kCols = 128 * NTL;   // columns per workgroup
-  __shared__ __align__(16) uint8_t atile[kTBM * kDownLD];
-  __shared__ __align__(16) uint8_t stage[4][64 * kStageLD];
-  __shared__ __align__(16) float scol[kBlock ? kCols / kGroup * KS : kCols];
+  constexpr int kSLD = 64 * KT + 16;   // LDS row stride of a staged weight tile (bytes)
+  constexpr int kCols = 128 * NTL;     // columns per workgroup
+  constexpr int KG = (KT + 1) / 2;     // 128-byte K groups (block-scale mode)
+  constexpr int kRuns = 2 * KT;        // 1 KB runs per wavefront and tile at most (32 rows * I bytes)
+  __shared__ __align__(16) uint8_t wst[2][64 * kSLD];
+  __shared__ __align__(16) uint8_t ost[4][64 * kStageLD];
+  __shared__ __align__(16) float scol[kBlock ? kCols / kGroup * KG : kCols];
   const int ng = (H + kCols - 1) / kCols;
   constexpr bool kComb = kOut == kCombineOut;
   const int tile = xcd_tile(blockIdx.x, (kComb ? comb_blocks : rows[0] / kTBM) * ng);
@@ -444,85 +457,83 @@ __global__ void __launch_bounds__(256, 2) down_wide_kernel(
   const int e = block_expert[b];
   if (e < 0) return;
   const int g = tile - bt * ng;
-  const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
-  const int r16 = lane & 15, kq = lane >> 4;
-  const int wt = wv & 1, wc = wv >> 1;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wt = wv & 1, wc = wv >> 1;   // row half, column stream
+  const int l32 = lane & 31, h = lane >> 5;
   const int nct = H / 64;
   const int sentinel = T * K1;
   const uint64_t magic = slot_div_magic(K1);
   const size_t nrows = (size_t)sentinel + 1;   // slot rows, with the padding rows' spare
   const int c0 = g * kCols;   // first column of the workgroup
 
-  // a_q rows of the block -> LDS, bytes [I, KS * 128) of each row zeroed: 4 * KS
-  // 16-byte chunks per thread, from unconditional (clamped) loads so that the
-  // unrolled copy issues them all before the first store waits
-  {
-    constexpr int cpr = KS * kGroup / 16;   // chunks per LDS row
+  // ---- the wavefront's a_q rows as B fragments, zero past I (K bytes ks * 64 + 32 h)
+  v8i aqf[2][KT];
+  const v8i zero8 = {0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
-    for (int i = 0; i < 4 * KS; ++i) {
-      const int c = tid + 256 * i, r = c / cpr, k = (c % cpr) * 16;
-      const uint4 v = *reinterpret_cast<const uint4*>(aq + ((size_t)b * kTBM + r) * I + (k < I ? k : 0));
-      const uint32_t msk = k < I ? 0xFFFFFFFFu : 0u;   // a per-word mask: a select of whole
-                                                       // uint4 values would go through scratch
-      *reinterpret_cast<uint4*>(&atile[r * kDownLD + k]) =
-          make_uint4(v.x & msk, v.y & msk, v.z & msk, v.w & msk);
-    }
+  for (int mt = 0; mt < 2; ++mt) {
+    const uint8_t* arow = aq + ((size_t)b * kTBM + 64 * wt + 32 * mt + l32) * I + 32 * h;
+#pragma unroll
+    for (int ks = 0; ks < KT; ++ks) aqf[mt][ks] = 64 * ks + 32 * h < I ? load32(arow + 64 * ks) : zero8;
   }
-  // w2 scales of the workgroup's columns -> LDS (per channel: kCols floats;
-  // block mode: per 128-column block and K step), clamped past H
+  // w2 scales of the workgroup's columns -> LDS (per channel: kCols floats; block mode:
+  // per 128-column block and K group), clamped past H
   if (!kBlock) {
 #pragma unroll
     for (int c = tid; c < kCols; c += 256) scol[c] = s2[(size_t)e * H + min(c0 + c, H - 1)];
-  } else if (tid < kCols / kGroup * KS) {
-    const int cb = min(c0 / kGroup + tid / KS, H / kGroup - 1);
-    scol[tid] = s2[((size_t)e * (H / kGroup) + cb) * (I / kGroup) + tid % KS];
+  } else if (tid < kCols / kGroup * KG) {
+    const int cb = min(c0 / kGroup + tid / KG, H / kGroup - 1);
+    scol[tid] = s2[((size_t)e * (H / kGroup) + cb) * (I / kGroup) + tid % KG];
   }
-  // this lane's rows: output scale in the MFMA layout (rows 64 wt + 16 m + r16)
-  // and slot ids in the store layout (rows 64 wt + 8 q + lane / 8)
-  float rsc[4], sar[4][KS];
+  // this lane's rows: output scale (and block-mode activation scales) in the MFMA layout
+  // (rows 64 wt + 32 mt + l32), slot ids in the store layout (rows 64 wt + 8 q + lane / 8)
+  float rsc[2], sar[2][KG];
 #pragma unroll
-  for (int m = 0; m < 4; ++m) {
-    const int p = b * kTBM + 64 * wt + 16 * m + r16;
-    rsc[m] = row_scale[p];
+  for (int mt = 0; mt < 2; ++mt) {
+    const int p = b * kTBM + 64 * wt + 32 * mt + l32;
+    rsc[mt] = row_scale[p];
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) sar[m][ks] = kBlock ? sa[(size_t)p * (I / kGroup) + ks] : 1.f;
+    for (int gk = 0; gk < KG; ++gk) sar[mt][gk] = kBlock ? sa[(size_t)p * (I / kGroup) + gk] : 1.f;
   }
   int srow[8];
 #pragma unroll
   for (int q = 0; q < 8; ++q)   // padding rows go to the spare row after the T*K1 slot rows
     srow[q] = min(sorted[b * kTBM + 64 * wt + 8 * q + (lane >> 3)], sentinel);
-  // K slices of this lane: bytes ks * 128 + kq * 32 .. +32. Weight slices past I
-  // are clamped to the row's first bytes (finite weights) and meet zeros in the
-  // a_q tile, so each such product is exactly 0.
-  uint32_t koff[KS];
+
+  // ---- weight tiles: the wavefront's half (rows 32 wt .. 32 wt + 31 of the tile, 32 I bytes)
+  // as 16-byte pieces at 1024 r + 16 lane; a tile past the last reads zeros
+  const int t0 = g * 2 * NTL + wc;   // this stream's first 64-column tile
+  const uint8_t* w2e = w2 + (size_t)e * H * I;
+  const int nrun = I / 32;           // 1 KB runs in 32 I bytes
+  u32x4_nt wr[kRuns];
+  auto wload = [&](int tj) __attribute__((always_inline)) {
+    const bool in = tj < nct;
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(w2e + (in ? (size_t)tj * 64 * I + (size_t)32 * wt * I : 0)), 0,
+        in ? 32 * I : 0, 0x00020000);
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
-    const int k = ks * kGroup + kq * 32;
-    koff[ks] = k < I ? k : 0;
-  }
-  int t = g * 2 * NTL + wc;   // this wavefront's first 64-column tile
-  const bool active = t < nct;
-  const int t0 = active ? t : 0;
-  // weight fragment rows: row r16 of MFMA tile n is column (r16/4)*16 + 4n + r16%4
-  const uint8_t* wb = w2 + (size_t)e * H * I + (size_t)((r16 >> 2) * 16 + (r16 & 3)) * I;
-  // two register sets of weight fragments: tile j computes from set j & 1 while the set
-  // of tile j + 1 is in flight, and set j & 1 is refilled with tile j + 2 as soon as its
-  // MFMAs have consumed it
-  v8i wf[2][4][KS];
-  auto wload = [&](v8i (&w)[4][KS], int tile) __attribute__((always_inline)) {
-#pragma unroll
-    for (int n = 0; n < 4; ++n)
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) w[n][ks] = load32(wb + (size_t)(tile * 64 + 4 * n) * I + koff[ks]);
+    for (int q = 0; q < kRuns; ++q)
+      if (q < nrun) wr[q] = __builtin_amdgcn_raw_buffer_load_b128(r, q * 1024 + lane * 16, 0, 2);
   };
-  wload(wf[0], t0);
-  if (NTL > 1) wload(wf[1], min(t0 + 2, nct - 1));
+  auto wstore = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int q = 0; q < kRuns; ++q)
+      if (q < nrun) {
+        const int o = 32 * wt * I + q * 1024 + lane * 16;   // byte of the tile's 64 * I
+        const int r = o / I, k = o - r * I;
+        *reinterpret_cast<u32x4_nt*>(&wst[wc][r * kSLD + k]) = wr[q];
+      }
+  };
+  // A-fragment row of lane l in a 32-row MFMA tile: the tile's output column
+  const int wcol = 16 * ((l32 >> 2) & 1) + 4 * (l32 >> 3) + (l32 & 3);
+
   // combining launch (one 64-column tile per wavefront): the slot rows that the first two
   // rows add do not depend on the GEMM, so their loads go out now
   static_assert(!kComb || NTL == 1, "the combining launch takes one tile per wavefront");
   const int nr = K1 - 1;
   const int last = nr > 0 ? nr - 1 : 0;
-  const int hs0 = t0 * 64 + (lane & 7) * 8;
+  const int tc0 = t0 < nct ? t0 : 0;
+  const int hs0 = tc0 * 64 + (lane & 7) * 8;
   const size_t cbase = (size_t)(hs0 >> 7) * nrows;   // the column block's first row
   const int hc = hs0 & 127;
   uint4 sv[2][2][8];
@@ -535,70 +546,92 @@ __global__ void __launch_bounds__(256, 2) down_wide_kernel(
         v[u][k] = *reinterpret_cast<const uint4*>(slot_out + (cbase + first + min(k, last)) * 128 + hc);
     }
   };
-  // (not with block scales over two K steps: their extra live registers would spill)
-  constexpr bool kEarly = kComb && !(kBlock && KS == 2);
-  if (kEarly) slot_issue(0, sv[0]);
-  __syncthreads();   // the a_q tile and the scales are in LDS
-  if (!active) return;
 
-  const v4f zero4 = {0.f, 0.f, 0.f, 0.f};
-  const uint8_t* trow = &atile[(64 * wt + r16) * kDownLD + kq * 32];
-  uint8_t* stg = stage[wv];
-#pragma unroll
+  wload(t0);
+  if (kComb) slot_issue(0, sv[0]);
+  const v16f zero16 = {};
+  uint8_t* stg = ost[wv];
+#pragma unroll 1
   for (int j = 0; j < NTL; ++j) {
-    const int cur = j & 1;
-    const int tj = t + 2 * j;
+    const int tj = t0 + 2 * j;
+    __syncthreads();   // the stream's buffer is free (the previous tile's fragments are read)
+    wstore();
+    if (j + 1 < NTL) wload(tj + 2);
+    __syncthreads();   // the tile is in LDS (and the scales, at j == 0)
+    // (H % 128 == 0 makes the tile count even, so both streams run out of tiles at the same j:
+    // the break is uniform over the workgroup and no barrier is left waiting)
     if (tj >= nct) break;
-    const int tl = min(tj + 4, nct - 1);   // the tile two steps ahead (re-read past the end)
-    v4f acc[4][4];   // [column tile n][row tile m]
+    v16f acc[2][2];   // [column tile ct][row tile mt]
 #pragma unroll
-    for (int n = 0; n < 4; ++n)
+    for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
-      for (int m = 0; m < 4; ++m) acc[n][m] = zero4;
+      for (int mt = 0; mt < 2; ++mt) acc[ct][mt] = zero16;
+    const uint8_t* wrow0 = &wst[wc][wcol * kSLD + 32 * h];
+    if (!kBlock) {
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      v8i tf[4];
+      for (int ks = 0; ks < KT; ++ks) {
+        const bool kin = 64 * ks + 32 * h < I;
 #pragma unroll
-      for (int m = 0; m < 4; ++m) tf[m] = load32(trow + 16 * m * kDownLD + ks * kGroup);
-      const float sb = kBlock ? scol[((tj * 64 - c0) / kGroup) * KS + ks] : 1.f;
+        for (int ct = 0; ct < 2; ++ct) {
+          const v8i wf = kin ? load32(wrow0 + 32 * ct * kSLD + 64 * ks) : zero8;
 #pragma unroll
-      for (int m = 0; m < 4; ++m)
+          for (int mt = 0; mt < 2; ++mt) acc[ct][mt] = mfma_32x32x64_fp8(wf, aqf[mt][ks], acc[ct][mt]);
+        }
+      }
+    } else {
+      // a 64-column tile lies in one 128-column block of w2's scales; one factor per
+      // lane, row tile and 128-byte K group
 #pragma unroll
-        for (int n = 0; n < 4; ++n) {
-          if (!kBlock) {
-            acc[n][m] = mfma_16x16x128_fp8(wf[cur][n][ks], tf[m], acc[n][m]);
-          } else {
-            const v4f p4 = mfma_16x16x128_fp8(wf[cur][n][ks], tf[m], zero4);
-            const float sc = sar[m][ks] * sb;
+      for (int gk = 0; gk < KG; ++gk) {
+        v16f t[2][2];
 #pragma unroll
-            for (int q = 0; q < 4; ++q) acc[n][m][q] += p4[q] * sc;
+        for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+          for (int mt = 0; mt < 2; ++mt) t[ct][mt] = zero16;
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+          const int ks = 2 * gk + kk;
+          if (ks >= KT) break;
+          const bool kin = 64 * ks + 32 * h < I;
+#pragma unroll
+          for (int ct = 0; ct < 2; ++ct) {
+            const v8i wf = kin ? load32(wrow0 + 32 * ct * kSLD + 64 * ks) : zero8;
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt) t[ct][mt] = mfma_32x32x64_fp8(wf, aqf[mt][ks], t[ct][mt]);
           }
         }
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    if (j + 2 < NTL) wload(wf[cur], tl);
-    __builtin_amdgcn_sched_barrier(0);
-    // scale, round and stage: lane (r16, kq) holds columns 16 kq .. 16 kq + 15 of
-    // rows 16 m + r16 of the wavefront's 64
-    float swc[16];
+        const float sb = scol[((tj * 64 - c0) / kGroup) * KG + gk];
 #pragma unroll
-    for (int c = 0; c < 16; c += 4) {
-      const float4 v = kBlock ? make_float4(1.f, 1.f, 1.f, 1.f)
-                              : *reinterpret_cast<const float4*>(&scol[tj * 64 - c0 + 16 * kq + c]);
-      swc[c] = v.x; swc[c + 1] = v.y; swc[c + 2] = v.z; swc[c + 3] = v.w;
-    }
+        for (int mt = 0; mt < 2; ++mt) {
+          const float f = sar[mt][gk] * sb;
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      uint32_t packed[8];
+          for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
-      for (int c = 0; c < 16; c += 2) {   // column c = 4 * n + q of this lane's 16
-        const float y0 = acc[c >> 2][m][c & 3] * swc[c] * rsc[m];
-        const float y1 = acc[(c + 1) >> 2][m][(c + 1) & 3] * swc[c + 1] * rsc[m];
-        packed[c >> 1] = pack_bf16x2(y0, y1);
+            for (int v = 0; v < 16; ++v) acc[ct][mt][v] += t[ct][mt][v] * f;
+        }
       }
-      uint4* sp = reinterpret_cast<uint4*>(stg + (16 * m + r16) * kStageLD + kq * 32);
-      sp[0] = make_uint4(packed[0], packed[1], packed[2], packed[3]);
-      sp[1] = make_uint4(packed[4], packed[5], packed[6], packed[7]);
+    }
+    // scale, round and stage: lane (l32, h) holds columns 32 ct + 16 h .. + 15 of row
+    // 32 mt + l32 of the wavefront's 64
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct) {
+      float swc[16];
+#pragma unroll
+      for (int c = 0; c < 16; c += 4) {
+        const float4 v = kBlock ? make_float4(1.f, 1.f, 1.f, 1.f)
+                                : *reinterpret_cast<const float4*>(&scol[tj * 64 - c0 + 32 * ct + 16 * h + c]);
+        swc[c] = v.x; swc[c + 1] = v.y; swc[c + 2] = v.z; swc[c + 3] = v.w;
+      }
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) {
+        uint32_t packed[8];
+#pragma unroll
+        for (int c = 0; c < 16; c += 2)
+          packed[c >> 1] = pack_bf16x2(acc[ct][mt][c] * swc[c] * rsc[mt], acc[ct][mt][c + 1] * swc[c + 1] * rsc[mt]);
+        uint4* sp = reinterpret_cast<uint4*>(stg + (32 * mt + l32) * kStageLD + (32 * ct + 16 * h) * 2);
+        sp[0] = make_uint4(packed[0], packed[1], packed[2], packed[3]);
+        sp[1] = make_uint4(packed[4], packed[5], packed[6], packed[7]);
+      }
     }
     // store: 8 lanes per row, 8 rows per instruction, each row's 128 bytes whole
     // (a wavefront's LDS operations complete in order, so no barrier is needed)
@@ -619,7 +652,6 @@ __global__ void __launch_bounds__(256, 2) down_wide_kernel(
       // (a row past the token's last is masked to +0.0, which leaves a sum that started
       // at +0.0 unchanged), slots 8.. one at a time. Padding rows read token 0's rows and
       // store nothing.
-      if (!kEarly) slot_issue(0, sv[0]);
 #pragma unroll
       for (int q = 0; q < 8; q += 2) {
         if (q + 2 < 8) slot_issue(q + 2, sv[((q >> 1) + 1) & 1]);
@@ -627,19 +659,19 @@ __global__ void __launch_bounds__(256, 2) down_wide_kernel(
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
           const int srw = srow[q + u];
-          float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+          float acs[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int k = 0; k < 8; ++k) {
             const uint32_t m = k < nr ? 0xFFFFFFFFu : 0u;
-            add_bf16x8(acc, make_uint4(v[u][k].x & m, v[u][k].y & m, v[u][k].z & m, v[u][k].w & m));
+            add_bf16x8(acs, make_uint4(v[u][k].x & m, v[u][k].y & m, v[u][k].z & m, v[u][k].w & m));
           }
           const int first = srw < sentinel ? srw - nr : 0;
           for (int k = 8; k < nr; ++k)
-            add_bf16x8(acc, *reinterpret_cast<const uint4*>(slot_out + (cbase + first + k) * 128 + hc));
-          add_bf16x8(acc, *reinterpret_cast<const uint4*>(stg + (8 * (q + u) + (lane >> 3)) * kStageLD + (lane & 7) * 16));
+            add_bf16x8(acs, *reinterpret_cast<const uint4*>(slot_out + (cbase + first + k) * 128 + hc));
+          add_bf16x8(acs, *reinterpret_cast<const uint4*>(stg + (8 * (q + u) + (lane >> 3)) * kStageLD + (lane & 7) * 16));
           if (srw < sentinel) {
-            const u32x4_nt nv = {pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]),
-                                 pack_bf16x2(acc[4], acc[5]), pack_bf16x2(acc[6], acc[7])};
+            const u32x4_nt nv = {pack_bf16x2(acs[0], acs[1]), pack_bf16x2(acs[2], acs[3]),
+                                 pack_bf16x2(acs[4], acs[5]), pack_bf16x2(acs[6], acs[7])};
             __builtin_nontemporal_store(nv, reinterpret_cast<u32x4_nt*>(out + (size_t)slot_token(srw, magic) * H + hs));
           }
         }
@@ -656,14 +688,18 @@ hipError_t launch_down_tile(const uint8_t* aq, const float* sa, const uint8_t* w
   const dim3 blk(256);
   if (I <= 2 * kGroup) {
     const dim3 grid(nb * ((H + 128 * kDownTiles - 1) / (128 * kDownTiles)));
-#define SRMOE_DOWN_WIDE(B, KS)                                                                        \
-  hipLaunchKernelGGL((down_wide_kernel<B, KS, kDownTiles, kRowsOut>), grid, blk, 0, stream, aq, sa, w2, s2, \
+#define SRMOE_DOWN_WIDE(B, KT)                                                                        \
+  hipLaunchKernelGGL((down_wide_kernel<B, KT, kDownTiles, kRowsOut>), grid, blk, 0, stream, aq, sa, w2, s2, \
                      sorted, block_expert, num_padded, row_scale, slot_out, T, H, I, K1, nullptr, 0)
-    if (I <= kGroup) {
-      if (block) SRMOE_DOWN_WIDE(true, 1); else SRMOE_DOWN_WIDE(false, 1);
-    } else {
-      if (block) SRMOE_DOWN_WIDE(true, 2); else SRMOE_DOWN_WIDE(false, 2);
+#define SRMOE_DOWN_WIDE2(KT) \
+  if (block) SRMOE_DOWN_WIDE(true, KT); else SRMOE_DOWN_WIDE(false, KT);
+    switch ((I + 63) / 64) {
+      case 1: SRMOE_DOWN_WIDE2(1) break;
+      case 2: SRMOE_DOWN_WIDE2(2) break;
+      case 3: SRMOE_DOWN_WIDE2(3) break;
+      default: SRMOE_DOWN_WIDE2(4) break;
     }
+#undef SRMOE_DOWN_WIDE2
 #undef SRMOE_DOWN_WIDE
     return hipGetLastError();
   }
@@ -696,22 +732,26 @@ hipError_t launch_down_wide_combine(const uint8_t* aq, const float* sa, const ui
   const dim3 blk(256);
   const dim3 grid(nb * ((H + 128 * kDownTiles - 1) / (128 * kDownTiles)));
   const dim3 grid_c(nbs * ((H + 128 * kCombTiles - 1) / (128 * kCombTiles)));
-#define SRMOE_DOWN_COMB(B, KS)                                                                          \
+#define SRMOE_DOWN_COMB(B, KT)                                                                          \
   do {                                                                                                  \
     if (parts & 1)                                                                                      \
-      hipLaunchKernelGGL((down_wide_kernel<B, KS, kDownTiles, kBlockedOut>), grid, blk, 0, stream, aq, sa, \
+      hipLaunchKernelGGL((down_wide_kernel<B, KT, kDownTiles, kBlockedOut>), grid, blk, 0, stream, aq, sa, \
                          w2, s2, sorted, block_expert, shared_first, row_scale, slot_out, T, H, I, K1,   \
                          nullptr, 0);                                                                   \
     if (parts & 2)                                                                                      \
-      hipLaunchKernelGGL((down_wide_kernel<B, KS, kCombTiles, kCombineOut>), grid_c, blk, 0, stream, aq, sa, \
+      hipLaunchKernelGGL((down_wide_kernel<B, KT, kCombTiles, kCombineOut>), grid_c, blk, 0, stream, aq, sa, \
                          w2, s2, sorted, block_expert, shared_first, row_scale, slot_out, T, H, I, K1, out, \
                          nbs);                                                                          \
   } while (0)
-  if (I <= kGroup) {
-    if (block) SRMOE_DOWN_COMB(true, 1); else SRMOE_DOWN_COMB(false, 1);
-  } else {
-    if (block) SRMOE_DOWN_COMB(true, 2); else SRMOE_DOWN_COMB(false, 2);
+#define SRMOE_DOWN_COMB2(KT) \
+  if (block) SRMOE_DOWN_COMB(true, KT); else SRMOE_DOWN_COMB(false, KT);
+  switch ((I + 63) / 64) {
+    case 1: SRMOE_DOWN_COMB2(1) break;
+    case 2: SRMOE_DOWN_COMB2(2) break;
+    case 3: SRMOE_DOWN_COMB2(3) break;
+    default: SRMOE_DOWN_COMB2(4) break;
   }
+#undef SRMOE_DOWN_COMB2
 #undef SRMOE_DOWN_COMB
   return hipGetLastError();
 }
