@@ -22,11 +22,11 @@ hipError_t launch_quant_x(const uint16_t*, int, int, bool, uint8_t*, float*, hip
 hipError_t launch_quant_a(const float*, int, int, bool, const int32_t*, const float*, int, const int32_t*,
                           uint8_t*, float*, float*, hipStream_t);
 hipError_t launch_gate_up(const uint8_t*, const float*, const uint8_t*, const float*, bool,
-                          const int32_t*, const int32_t*, const int32_t*, float*, int, int, int, int,
-                          int, int, hipStream_t);
+                          const int32_t*, const int32_t*, const int32_t*, const int32_t*, float*, int, int,
+                          int, int, int, int, hipStream_t);
 hipError_t launch_down(const uint8_t*, const float*, const uint8_t*, const float*, bool,
-                       const int32_t*, const int32_t*, const int32_t*, const float*, uint16_t*, int,
-                       int, int, int, int, int, hipStream_t);
+                       const int32_t*, const int32_t*, const int32_t*, const int32_t*, const float*,
+                       uint16_t*, int, int, int, int, int, int, hipStream_t);
 hipError_t launch_combine(const uint16_t*, const uint16_t*, int, int, int, uint16_t*, hipStream_t);
 bool down_wide_supported(int I);
 hipError_t launch_down_wide_combine(const uint8_t*, const float*, const uint8_t*, const float*, bool,
@@ -271,7 +271,7 @@ int moe_ffn_gate_up(const uint8_t* w13, const float* s13, int scale_mode, int T,
                                             as_stream(stream)));
   return hip_status(launch_gate_up(reinterpret_cast<const uint8_t*>(ws + L.xq),
                                    reinterpret_cast<const float*>(ws + L.sx), w13, s13, blk,
-                                   sorted_slot_ids, block_expert, num_padded,
+                                   sorted_slot_ids, block_expert, num_padded, nullptr,
                                    reinterpret_cast<float*>(ws + L.a), T, H, I, E1, K1, block_m,
                                    as_stream(stream)));
 }
@@ -301,7 +301,7 @@ int moe_ffn_down(const uint8_t* w2, const float* s2, int scale_mode, int T, int 
   if (e != hipSuccess) return hip_status(e);
   return hip_status(launch_down(reinterpret_cast<const uint8_t*>(ws + L.aq),
                                 reinterpret_cast<const float*>(ws + L.sa), w2, s2, blk,
-                                sorted_slot_ids, block_expert, num_padded,
+                                sorted_slot_ids, block_expert, num_padded, nullptr,
                                 reinterpret_cast<const float*>(ws + L.rs),
                                 reinterpret_cast<uint16_t*>(ws + L.slot_out), T, H, I, E1, K1,
                                 block_m, as_stream(stream)));
@@ -449,8 +449,12 @@ static int layer_forward(const uint16_t* x, const LogitSrc& src, const void* log
   if (block_m == 128) {
     // prefill shapes: gate/up, the FP8 quantisation of a, then the down GEMM
     const int P_max = (int)sorted_capacity(T, K1, E1, block_m);
-    st = mark(moe_ffn_gate_up(w13, s13, scale_mode, T, H, I, E1, K1, block_m, sorted_slot_ids, block_expert,
-                              num_padded, ffn_ws, ffn_ws_bytes, stream),
+    // (the tiles of one expert grouped by the align's offsets, so that its blocks share the
+    // weight slices through L2)
+    st = mark(hip_status(launch_gate_up(reinterpret_cast<const uint8_t*>(ws + L.xq),
+                                        reinterpret_cast<const float*>(ws + L.sx), w13, s13, blk, sorted_slot_ids,
+                                        block_expert, num_padded, expert_offsets,
+                                        reinterpret_cast<float*>(ws + L.a), T, H, I, E1, K1, block_m, sm)),
               "gate_up");
     if (st != SRMOE_OK) return st;
     st = mark(hip_status(launch_quant_a(reinterpret_cast<const float*>(ws + L.a), P_max, I, blk, sorted_slot_ids,
@@ -463,7 +467,8 @@ static int layer_forward(const uint16_t* x, const LogitSrc& src, const void* log
       // I > 256: the K-looped down GEMM, then the combine
       st = mark(hip_status(launch_down(reinterpret_cast<const uint8_t*>(ws + L.aq),
                                        reinterpret_cast<const float*>(ws + L.sa), w2, s2, blk, sorted_slot_ids,
-                                       block_expert, num_padded, reinterpret_cast<const float*>(ws + L.rs),
+                                       block_expert, num_padded, expert_offsets,
+                                       reinterpret_cast<const float*>(ws + L.rs),
                                        reinterpret_cast<uint16_t*>(ws + L.slot_out), T, H, I, E1, K1, block_m,
                                        sm)),
                 "down");
@@ -476,7 +481,7 @@ static int layer_forward(const uint16_t* x, const LogitSrc& src, const void* log
     for (int part = 1; part <= 2; ++part) {
       st = mark(hip_status(launch_down_wide_combine(
                     reinterpret_cast<const uint8_t*>(ws + L.aq), reinterpret_cast<const float*>(ws + L.sa), w2,
-                    s2, blk, sorted_slot_ids, block_expert, expert_offsets + E,
+                    s2, blk, sorted_slot_ids, block_expert, expert_offsets,
                     reinterpret_cast<const float*>(ws + L.rs), reinterpret_cast<uint16_t*>(ws + L.slot_out), out,
                     T, H, I, E1, K1, part, sm)),
                 part == 1 ? "down_routed" : "down_shared_combine");

@@ -165,6 +165,23 @@ __device__ __forceinline__ int xcd_tile(int i, int n) {
   return x * q + (x < r ? x : r) + j;
 }
 
+// Tile t (0 <= t < used blocks * ny, in the order xcd_tile walks) -> (row block, column
+// tile) with the tiles of one expert grouped column tile by column tile: the ny tiles of
+// each of the expert's nb_e blocks occupy the same range of t as in row-block-major order,
+// but inside it the expert's blocks take each column tile back to back. Those tiles read the
+// same weight slice at the same time, so one XCD's L2 serves it to all of them (in row-block
+// order the same slice comes back ny tiles later, after it has left the L2). block_expert and
+// expert_offsets are the align outputs (offsets in rows, multiples of block_m).
+__device__ __forceinline__ void grouped_tile(int t, int ny, int block_m, const int32_t* __restrict__ block_expert,
+                                             const int32_t* __restrict__ expert_offsets, int* b, int* cy) {
+  const int e = block_expert[t / ny];
+  const int b0 = expert_offsets[e] / block_m;
+  const int nbe = expert_offsets[e + 1] / block_m - b0;
+  const int u = t - b0 * ny;
+  *cy = u / nbe;
+  *b = b0 + (u - *cy * nbe);
+}
+
 // Token of sorted slot id s = t * K1 + k, i.e. floor(s / K1), as a multiply by
 // magic = ceil(2^32 / K1) (slot_div_magic). Exact for K1 <= 16 and s <= 2^24:
 // the error term s * (magic * K1 - 2^32) / (K1 * 2^32) stays below 1 / (16 K1).

@@ -255,17 +255,18 @@ static hipError_t launch_gate_up_t(int block_m, dim3 grid, hipStream_t st, const
 }
 
 hipError_t launch_gate_up_tile(const uint8_t*, const float*, const uint8_t*, const float*, bool,
-                               const int32_t*, const int32_t*, const int32_t*, float*, int, int, int,
-                               int, int, hipStream_t);
+                               const int32_t*, const int32_t*, const int32_t*, const int32_t*, float*, int,
+                               int, int, int, int, hipStream_t);
 
 // block_m 32..128 (block_m 16 uses launch_gate_up_decode; 128 the LDS-tiled kernel).
+// expert_offsets (block_m 128; may be null): group the tiles of one expert (grouped_tile).
 hipError_t launch_gate_up(const uint8_t* xq, const float* sx, const uint8_t* w13, const float* s13,
                           bool block, const int32_t* sorted, const int32_t* block_expert,
-                          const int32_t* num_padded, float* a, int T, int H, int I, int E1, int K1,
-                          int block_m, hipStream_t stream) {
+                          const int32_t* num_padded, const int32_t* expert_offsets, float* a, int T, int H,
+                          int I, int E1, int K1, int block_m, hipStream_t stream) {
   if (block_m == 128)
-    return launch_gate_up_tile(xq, sx, w13, s13, block, sorted, block_expert, num_padded, a, T, H, I,
-                               E1, K1, stream);
+    return launch_gate_up_tile(xq, sx, w13, s13, block, sorted, block_expert, num_padded, expert_offsets, a, T,
+                               H, I, E1, K1, stream);
   const int P_max = (int)sorted_capacity(T, K1, E1, block_m);
   const dim3 grid(P_max / block_m, (I + 63) / 64);
   return block ? launch_gate_up_t<true>(block_m, grid, stream, xq, sx, w13, s13, sorted, block_expert, a, T, H, I, K1)
@@ -287,8 +288,8 @@ static hipError_t launch_down_t(int block_m, dim3 grid, hipStream_t st, const ui
 }
 
 hipError_t launch_down_tile(const uint8_t*, const float*, const uint8_t*, const float*, bool,
-                            const int32_t*, const int32_t*, const int32_t*, const float*, uint16_t*,
-                            int, int, int, int, int, hipStream_t);
+                            const int32_t*, const int32_t*, const int32_t*, const int32_t*, const float*,
+                            uint16_t*, int, int, int, int, int, hipStream_t);
 
 bool down_decode_supported(int I);
 hipError_t launch_down_decode(const uint8_t*, const float*, const uint8_t*, const float*, bool,
@@ -297,10 +298,10 @@ hipError_t launch_down_decode(const uint8_t*, const float*, const uint8_t*, cons
 
 hipError_t launch_down(const uint8_t* aq, const float* sa, const uint8_t* w2, const float* s2,
                        bool block, const int32_t* sorted, const int32_t* block_expert,
-                       const int32_t* num_padded, const float* row_scale, uint16_t* slot_out, int T,
-                       int H, int I, int E1, int K1, int block_m, hipStream_t stream) {
+                       const int32_t* num_padded, const int32_t* expert_offsets, const float* row_scale,
+                       uint16_t* slot_out, int T, int H, int I, int E1, int K1, int block_m, hipStream_t stream) {
   if (block_m == 128)
-    return launch_down_tile(aq, sa, w2, s2, block, sorted, block_expert, num_padded, row_scale,
+    return launch_down_tile(aq, sa, w2, s2, block, sorted, block_expert, num_padded, expert_offsets, row_scale,
                             slot_out, T, H, I, E1, K1, stream);
   if (block_m == 16 && down_decode_supported(I))
     return launch_down_decode(aq, sa, w2, s2, block, sorted, block_expert, row_scale, slot_out, T,

@@ -34,16 +34,18 @@ __global__ void __launch_bounds__(256, 2) gate_up_tile_kernel(
     const uint8_t* __restrict__ xq, const float* __restrict__ sx, const uint8_t* __restrict__ w13,
     const float* __restrict__ s13, const int32_t* __restrict__ sorted,
     const int32_t* __restrict__ block_expert, const int32_t* __restrict__ num_padded,
-    float* __restrict__ a_out, int T, int H, int I, int K1) {
+    const int32_t* __restrict__ expert_offsets, float* __restrict__ a_out, int T, int H, int I, int K1) {
   __shared__ __align__(16) uint8_t lds[2][kTile];
-  // tiles (row block, 64-column group) in row-block-major order, walked per XCD
+  // tiles (row block, 64-column group) walked per XCD: grouped by expert when the offsets
+  // are given (grouped_tile), else in row-block-major order
   const int ny = (I + 63) / 64;
   const int tile = xcd_tile(blockIdx.x, num_padded[0] / kTBM * ny);
   if (tile < 0) return;
-  const int b = tile / ny;
+  int b = tile / ny, cy = tile - b * ny;
+  if (expert_offsets) grouped_tile(tile, ny, kTBM, block_expert, expert_offsets, &b, &cy);
   const int e = block_expert[b];
   if (e < 0) return;
-  const int c0 = (tile - b * ny) * 64;  // first intermediate column of this workgroup
+  const int c0 = cy * 64;  // first intermediate column of this workgroup
   const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
   const int r16 = lane & 15, kq = lane >> 4;
   const int wm = wv >> 1, wn = wv & 1;
@@ -227,16 +229,17 @@ __global__ void __launch_bounds__(256, 2) down_tile_kernel(
     const uint8_t* __restrict__ aq, const float* __restrict__ sa, const uint8_t* __restrict__ w2,
     const float* __restrict__ s2, const int32_t* __restrict__ sorted,
     const int32_t* __restrict__ block_expert, const int32_t* __restrict__ num_padded,
-    const float* __restrict__ row_scale, uint16_t* __restrict__ slot_out, int T, int H, int I,
-    int K1) {
+    const int32_t* __restrict__ expert_offsets, const float* __restrict__ row_scale,
+    uint16_t* __restrict__ slot_out, int T, int H, int I, int K1) {
   __shared__ __align__(16) uint8_t lds[2][kTile];   // rows 0..127 weights (h), 128..255 a_q rows
   const int ny = H / 128;
   const int tile = xcd_tile(blockIdx.x, num_padded[0] / kTBM * ny);
   if (tile < 0) return;
-  const int b = tile / ny;
+  int b = tile / ny, cy = tile - b * ny;
+  if (expert_offsets) grouped_tile(tile, ny, kTBM, block_expert, expert_offsets, &b, &cy);
   const int e = block_expert[b];
   if (e < 0) return;
-  const int h0 = (tile - b * ny) * 128;
+  const int h0 = cy * 128;
   const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
   const int r16 = lane & 15, kq = lane >> 4;
   const int wh = wv >> 1, wt = wv & 1;   // 64-column half, 64-token half
@@ -439,8 +442,8 @@ __global__ void __launch_bounds__(256, 2) down_wide_kernel(
     const uint8_t* __restrict__ aq, const float* __restrict__ sa, const uint8_t* __restrict__ w2,
     const float* __restrict__ s2, const int32_t* __restrict__ sorted,
     const int32_t* __restrict__ block_expert, const int32_t* __restrict__ rows,
-    const float* __restrict__ row_scale, uint16_t* __restrict__ slot_out, int T, int H, int I,
-    int K1, uint16_t* __restrict__ out, int comb_blocks) {
+    const int32_t* __restrict__ expert_offsets, const float* __restrict__ row_scale,
+    uint16_t* __restrict__ slot_out, int T, int H, int I, int K1, uint16_t* __restrict__ out, int comb_blocks) {
   constexpr int kSLD = 64 * KT + 16;   // LDS row stride of a staged weight tile (bytes)
   constexpr int kCols = 128 * NTL;     // columns per workgroup
   constexpr int KG = (KT + 1) / 2;     // 128-byte K groups (block-scale mode)
@@ -452,11 +455,20 @@ __global__ void __launch_bounds__(256, 2) down_wide_kernel(
   constexpr bool kComb = kOut == kCombineOut;
   const int tile = xcd_tile(blockIdx.x, (kComb ? comb_blocks : rows[0] / kTBM) * ng);
   if (tile < 0) return;
-  const int bt = tile / ng;
+  // with the offsets: the routed rows grouped by expert (grouped_tile), the combining
+  // launch's blocks (all the shared expert's) column group by column group
+  int bt = tile / ng, g = tile - bt * ng;
+  if (expert_offsets) {
+    if (kComb) {
+      g = tile / comb_blocks;
+      bt = tile - g * comb_blocks;
+    } else {
+      grouped_tile(tile, ng, kTBM, block_expert, expert_offsets, &bt, &g);
+    }
+  }
   const int b = kComb ? rows[0] / kTBM + bt : bt;
   const int e = block_expert[b];
   if (e < 0) return;
-  const int g = tile - bt * ng;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wt = wv & 1, wc = wv >> 1;   // row half, column stream
@@ -682,15 +694,15 @@ __global__ void __launch_bounds__(256, 2) down_wide_kernel(
 
 hipError_t launch_down_tile(const uint8_t* aq, const float* sa, const uint8_t* w2, const float* s2,
                             bool block, const int32_t* sorted, const int32_t* block_expert,
-                            const int32_t* num_padded, const float* row_scale, uint16_t* slot_out,
-                            int T, int H, int I, int E1, int K1, hipStream_t stream) {
+                            const int32_t* num_padded, const int32_t* expert_offsets, const float* row_scale,
+                            uint16_t* slot_out, int T, int H, int I, int E1, int K1, hipStream_t stream) {
   const int nb = (int)(sorted_capacity(T, K1, E1, kTBM) / kTBM);
   const dim3 blk(256);
   if (I <= 2 * kGroup) {
     const dim3 grid(nb * ((H + 128 * kDownTiles - 1) / (128 * kDownTiles)));
 #define SRMOE_DOWN_WIDE(B, KT)                                                                        \
   hipLaunchKernelGGL((down_wide_kernel<B, KT, kDownTiles, kRowsOut>), grid, blk, 0, stream, aq, sa, w2, s2, \
-                     sorted, block_expert, num_padded, row_scale, slot_out, T, H, I, K1, nullptr, 0)
+                     sorted, block_expert, num_padded, expert_offsets, row_scale, slot_out, T, H, I, K1, nullptr, 0)
 #define SRMOE_DOWN_WIDE2(KT) \
   if (block) SRMOE_DOWN_WIDE(true, KT); else SRMOE_DOWN_WIDE(false, KT);
     switch ((I + 63) / 64) {
@@ -706,10 +718,10 @@ hipError_t launch_down_tile(const uint8_t* aq, const float* sa, const uint8_t* w
   const dim3 grid(nb * (H / 128));
   if (block)
     hipLaunchKernelGGL(down_tile_kernel<true>, grid, blk, 0, stream, aq, sa, w2, s2, sorted,
-                       block_expert, num_padded, row_scale, slot_out, T, H, I, K1);
+                       block_expert, num_padded, expert_offsets, row_scale, slot_out, T, H, I, K1);
   else
     hipLaunchKernelGGL(down_tile_kernel<false>, grid, blk, 0, stream, aq, sa, w2, s2, sorted,
-                       block_expert, num_padded, row_scale, slot_out, T, H, I, K1);
+                       block_expert, num_padded, expert_offsets, row_scale, slot_out, T, H, I, K1);
   return hipGetLastError();
 }
 
@@ -722,9 +734,10 @@ bool down_wide_supported(int I) { return I <= 2 * kGroup; }
 // rows are never written.
 hipError_t launch_down_wide_combine(const uint8_t* aq, const float* sa, const uint8_t* w2, const float* s2,
                                     bool block, const int32_t* sorted, const int32_t* block_expert,
-                                    const int32_t* shared_first, const float* row_scale,
+                                    const int32_t* expert_offsets, const float* row_scale,
                                     uint16_t* slot_out, uint16_t* out, int T, int H, int I, int E1, int K1,
                                     int parts, hipStream_t stream) {
+  const int32_t* shared_first = expert_offsets + (E1 - 1);   // the shared expert's first row
   // parts: bit 0 the routed experts' launch, bit 1 the shared expert's launch with the combine
   if (!down_wide_supported(I)) return hipErrorInvalidValue;
   const int nb = (int)(sorted_capacity(T, K1, E1, kTBM) / kTBM);
@@ -736,12 +749,12 @@ hipError_t launch_down_wide_combine(const uint8_t* aq, const float* sa, const ui
   do {                                                                                                  \
     if (parts & 1)                                                                                      \
       hipLaunchKernelGGL((down_wide_kernel<B, KT, kDownTiles, kBlockedOut>), grid, blk, 0, stream, aq, sa, \
-                         w2, s2, sorted, block_expert, shared_first, row_scale, slot_out, T, H, I, K1,   \
-                         nullptr, 0);                                                                   \
+                         w2, s2, sorted, block_expert, shared_first, expert_offsets, row_scale, slot_out, T, \
+                         H, I, K1, nullptr, 0);                                                         \
     if (parts & 2)                                                                                      \
       hipLaunchKernelGGL((down_wide_kernel<B, KT, kCombTiles, kCombineOut>), grid_c, blk, 0, stream, aq, sa, \
-                         w2, s2, sorted, block_expert, shared_first, row_scale, slot_out, T, H, I, K1, out, \
-                         nbs);                                                                          \
+                         w2, s2, sorted, block_expert, shared_first, expert_offsets, row_scale, slot_out, T, \
+                         H, I, K1, out, nbs);                                                           \
   } while (0)
 #define SRMOE_DOWN_COMB2(KT) \
   if (block) SRMOE_DOWN_COMB(true, KT); else SRMOE_DOWN_COMB(false, KT);
@@ -758,16 +771,17 @@ hipError_t launch_down_wide_combine(const uint8_t* aq, const float* sa, const ui
 
 hipError_t launch_gate_up_tile(const uint8_t* xq, const float* sx, const uint8_t* w13,
                                const float* s13, bool block, const int32_t* sorted,
-                               const int32_t* block_expert, const int32_t* num_padded, float* a,
-                               int T, int H, int I, int E1, int K1, hipStream_t stream) {
+                               const int32_t* block_expert, const int32_t* num_padded,
+                               const int32_t* expert_offsets, float* a, int T, int H, int I, int E1, int K1,
+                               hipStream_t stream) {
   const int nb = (int)(sorted_capacity(T, K1, E1, kTBM) / kTBM);
   const dim3 grid(nb * ((I + 63) / 64));
   if (block)
     hipLaunchKernelGGL(gate_up_tile_kernel<true>, grid, dim3(256), 0, stream, xq, sx, w13, s13,
-                       sorted, block_expert, num_padded, a, T, H, I, K1);
+                       sorted, block_expert, num_padded, expert_offsets, a, T, H, I, K1);
   else
     hipLaunchKernelGGL(gate_up_tile_kernel<false>, grid, dim3(256), 0, stream, xq, sx, w13, s13,
-                       sorted, block_expert, num_padded, a, T, H, I, K1);
+                       sorted, block_expert, num_padded, expert_offsets, a, T, H, I, K1);
   return hipGetLastError();
 }
 
