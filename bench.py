@@ -56,6 +56,15 @@ TRAFFIC_PROFILES = {
                              "shared_routed_expert_amd/csrc/common.hpp"]),
     ("prefill", "gate_up"): ("profiles/gate_up_tile_prefill_T4096_hbm_traffic.txt",
                              ["shared_routed_expert_amd/csrc/ffn_tile.hip", "shared_routed_expert_amd/csrc/common.hpp"]),
+    ("prefill16k_zipf", "gate_up"): ("profiles/gate_up_tile_prefill16k_zipf_hbm_traffic.txt",
+                                     ["shared_routed_expert_amd/csrc/ffn_tile.hip",
+                                      "shared_routed_expert_amd/csrc/common.hpp"]),
+    ("prefill16k_zipf", "down_routed"): ("profiles/down_routed_prefill16k_zipf_hbm_traffic.txt",
+                                         ["shared_routed_expert_amd/csrc/ffn_tile.hip",
+                                          "shared_routed_expert_amd/csrc/common.hpp"]),
+    ("unsharded_block", "gate_up"): ("profiles/gate_up_tile_unsharded_block_T4096_hbm_traffic.txt",
+                                     ["shared_routed_expert_amd/csrc/ffn_tile.hip",
+                                      "shared_routed_expert_amd/csrc/common.hpp"]),
 }
 
 
