@@ -10,7 +10,11 @@
 // rows a fragment read touches land on distinct banks.
 //
 // gate_up: grid (P_max / 128, ceil(I / 64)); epilogue as in the other gate_up
-// kernels: a = silu(g) * u in float32 per sorted row (0 for padding rows).
+// kernels: a = silu(g) * u in float32 per sorted row (0 for padding rows). In block
+// mode every K step's products are rescaled by (x scale x weight block scale) before
+// they are accumulated; there the weights are the MFMA's A operand, so that a lane's 4
+// results share one token and one weight block and the rescale takes one product per
+// tile (per channel, the x rows are A and the scales are applied once, in the epilogue).
 // down: grid (P_max / 128, H / 128); the same double-buffered K loop over
 // K = I (a partial last step is zero-filled in LDS) with the weights as the
 // MFMA A operand, so D holds [column][token]; inside a wavefront's 64 columns
@@ -146,14 +150,16 @@ __global__ void __launch_bounds__(256, 2) gate_up_tile_kernel(
       _Pragma("unroll") for (int n = 0; n < 4; ++n)                                            \
         acc[m][n] = mfma_16x16x128_fp8(af[m], bf[n], acc[m][n]);                               \
     } else {                                                                                   \
+      /* weights as the A operand: the lane's 4 results are 4 weight rows of one token, so the \
+         step's rescale is one product of the token's and the tile's scale per tile */         \
       const float4 sw = *reinterpret_cast<const float4*>(&scl[buf][kTBM + 4 * wn]);            \
       const float swn[4] = {sw.x, sw.y, sw.z, sw.w};                                           \
       _Pragma("unroll") for (int m = 0; m < 4; ++m) {                                          \
-        const float4 sv = *reinterpret_cast<const float4*>(&scl[buf][64 * wm + 16 * m + 4 * kq]); \
-        const float sxv[4] = {sv.x, sv.y, sv.z, sv.w};                                         \
+        const float sxm = scl[buf][64 * wm + 16 * m + r16];                                    \
         _Pragma("unroll") for (int n = 0; n < 4; ++n) {                                        \
-          const v4f t = mfma_16x16x128_fp8(af[m], bf[n], zero4);                               \
-          _Pragma("unroll") for (int j = 0; j < 4; ++j) acc[m][n][j] += t[j] * (sxv[j] * swn[n]); \
+          const v4f t = mfma_16x16x128_fp8(bf[n], af[m], zero4);                               \
+          const float sc = sxm * swn[n];                                                       \
+          _Pragma("unroll") for (int j = 0; j < 4; ++j) acc[m][n][j] += t[j] * sc;             \
         }                                                                                      \
       }                                                                                        \
     }                                                                                          \
@@ -187,7 +193,30 @@ __global__ void __launch_bounds__(256, 2) gate_up_tile_kernel(
 #undef SRMOE_TILE_LSTORE
 
   // epilogue: gate tile n pairs with up tile n + 2 (same intermediate columns).
-  // Tokens of this lane's output rows (-1 for padding rows) are re-read here
+  if (kBlock) {
+    // block mode (weights were the A operand): element j of tile (m, n) is intermediate
+    // column c0 + 32 wn + 16 n + 4 kq + j of token row 64 wm + 16 m + r16, already scaled;
+    // each lane stores 4 consecutive columns (I % 128 == 0: every column exists)
+    bool valid[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) valid[m] = sorted[b * kTBM + 64 * wm + 16 * m + r16] < sentinel;
+#pragma unroll
+    for (int n = 0; n < 2; ++n) {
+      const int col = c0 + 32 * wn + 16 * n + 4 * kq;
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const int p = b * kTBM + 64 * wm + 16 * m + r16;
+        float4 av;
+        av.x = valid[m] ? silu(acc[m][n][0]) * acc[m][n + 2][0] : 0.f;
+        av.y = valid[m] ? silu(acc[m][n][1]) * acc[m][n + 2][1] : 0.f;
+        av.z = valid[m] ? silu(acc[m][n][2]) * acc[m][n + 2][2] : 0.f;
+        av.w = valid[m] ? silu(acc[m][n][3]) * acc[m][n + 2][3] : 0.f;
+        *reinterpret_cast<float4*>(a_out + (size_t)p * I + col) = av;
+      }
+    }
+    return;
+  }
+  // per channel: tokens of this lane's output rows (-1 for padding rows) are re-read here
   // rather than held through the K loop; all scales are fetched before any is used.
   int otok[4][4];
 #pragma unroll
@@ -201,12 +230,12 @@ __global__ void __launch_bounds__(256, 2) gate_up_tile_kernel(
 #pragma unroll
   for (int m = 0; m < 4; ++m)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) sxo[m][j] = kBlock ? 1.f : sx[max(otok[m][j], 0)];
+    for (int j = 0; j < 4; ++j) sxo[m][j] = sx[max(otok[m][j], 0)];
 #pragma unroll
   for (int n = 0; n < 2; ++n) {
     const int colc = min(c0 + 32 * wn + 16 * n + r16, I - 1);
-    sg[n] = kBlock ? 1.f : s13[(size_t)e * 2 * I + colc];
-    su[n] = kBlock ? 1.f : s13[(size_t)e * 2 * I + I + colc];
+    sg[n] = s13[(size_t)e * 2 * I + colc];
+    su[n] = s13[(size_t)e * 2 * I + I + colc];
   }
 #pragma unroll
   for (int n = 0; n < 2; ++n) {
