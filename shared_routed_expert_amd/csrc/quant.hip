@@ -21,7 +21,7 @@ __global__ void __launch_bounds__(256) quant_x_kernel(const uint16_t* __restrict
 // It also writes each sorted row's output scale for the down GEMM: the row's
 // routing weight topk_w[s] (0 for padding rows), times the row's FP8 scale in
 // per-channel mode. One 256-thread workgroup per 16 rows, 16 threads (one DPP
-// row) per sorted row; each thread takes 2 consecutive values per 32-wide stripe.
+// row) per sorted row; each thread takes 4 consecutive values per 64-wide stripe.
 template <bool kBlock>
 __global__ void __launch_bounds__(256) quant_a_kernel(const float* __restrict__ a, int I,
                                                       const int32_t* __restrict__ sorted,
@@ -73,20 +73,35 @@ __global__ void __launch_bounds__(256) quant_a_kernel(const float* __restrict__ 
     }
   } else {
     if (part == 0) row_scale[p] = wgt;
-    for (int g = 0; g < I; g += kGroup) {
-      float2 v[4];
-      float amax = 0.0f;
+    // 128-column groups in batches of 4, every load of a batch issued before any is used;
+    // a group is the row's 16 threads x 2 float4 (columns g + 4 part + 64 j)
+    constexpr int kBatch = 4;
+    for (int g0 = 0; g0 < I; g0 += kBatch * kGroup) {
+      float4 v[kBatch][2];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        v[j] = *reinterpret_cast<const float2*>(row + g + part * 2 + 32 * j);
-        amax = fmaxf(amax, fmaxf(fabsf(v[j].x), fabsf(v[j].y)));
+      for (int b = 0; b < kBatch; ++b) {
+        const int g = g0 + b * kGroup;
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          v[b][j] = g < I ? *reinterpret_cast<const float4*>(row + g + part * 4 + 64 * j)
+                          : make_float4(0.f, 0.f, 0.f, 0.f);
       }
-      const float scale = fp8_scale(row16_max(amax));
-      if (part == 0) sa[(size_t)p * (I / kGroup) + g / kGroup] = scale;
-      const ScaleDiv q = scale_div(scale);
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        *reinterpret_cast<uint16_t*>(qrow + g + part * 2 + 32 * j) = (uint16_t)quant2(q, v[j].x, v[j].y);
+      for (int b = 0; b < kBatch; ++b) {
+        const int g = g0 + b * kGroup;
+        if (g >= I) break;
+        float amax = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v[b][j].x), fabsf(v[b][j].y)), fmaxf(fabsf(v[b][j].z), fabsf(v[b][j].w))));
+        const float scale = fp8_scale(row16_max(amax));
+        if (part == 0) sa[(size_t)p * (I / kGroup) + g / kGroup] = scale;
+        const ScaleDiv q = scale_div(scale);
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          *reinterpret_cast<uint32_t*>(qrow + g + part * 4 + 64 * j) =
+              quant2(q, v[b][j].x, v[b][j].y) | (quant2(q, v[b][j].z, v[b][j].w) << 16);
+      }
     }
   }
 }
