@@ -430,6 +430,7 @@ __global__ void __launch_bounds__(256, 2) down_tile_kernel(
 //    read once by the combine, and whole-line streaming stores keep it from evicting the
 //    w2 tiles that the block's neighbours re-read from L2.
 constexpr int kDownTiles = 4;
+constexpr int kDownTilesWide = 10;         // 1,280 columns per workgroup (down_wide_tiles_wide)
 constexpr int kCombTiles = 1;              // 64-column tiles per wavefront in the combining launch
 constexpr int kStageLD = 128 + 16;         // LDS row stride of an output staging buffer
 
@@ -721,6 +722,17 @@ __global__ void __launch_bounds__(256, 2) down_wide_kernel(
   }
 }
 
+// Column tiles per down_wide workgroup. 128 rows x 512 columns while the routed rows give
+// few row blocks; 1,280 columns once that width still leaves four full rounds of resident
+// workgroups (2 per CU). The wider workgroup spreads its prologue (a_q fragments, scales,
+// slot ids) over 2.5x the columns; the narrower one keeps the last round short. Measured at
+// H = 5120, I = 192: 4,096 tokens 120 us (4) against 127 us (10); 16k tokens 406 us
+// against 364 us.
+static bool down_wide_tiles_wide(int T, int H, int K1) {
+  const size_t blocks = (size_t)T * K1 / kTBM;
+  return blocks * ((H + 128 * kDownTilesWide - 1) / (128 * kDownTilesWide)) >= 2048;
+}
+
 hipError_t launch_down_tile(const uint8_t* aq, const float* sa, const uint8_t* w2, const float* s2,
                             bool block, const int32_t* sorted, const int32_t* block_expert,
                             const int32_t* num_padded, const int32_t* expert_offsets, const float* row_scale,
@@ -728,12 +740,20 @@ hipError_t launch_down_tile(const uint8_t* aq, const float* sa, const uint8_t* w
   const int nb = (int)(sorted_capacity(T, K1, E1, kTBM) / kTBM);
   const dim3 blk(256);
   if (I <= 2 * kGroup) {
-    const dim3 grid(nb * ((H + 128 * kDownTiles - 1) / (128 * kDownTiles)));
-#define SRMOE_DOWN_WIDE(B, KT)                                                                        \
-  hipLaunchKernelGGL((down_wide_kernel<B, KT, kDownTiles, kRowsOut>), grid, blk, 0, stream, aq, sa, w2, s2, \
+    const bool wide = down_wide_tiles_wide(T, H, K1);
+    const int ntl = wide ? kDownTilesWide : kDownTiles;
+    const dim3 grid(nb * ((H + 128 * ntl - 1) / (128 * ntl)));
+#define SRMOE_DOWN_WIDE(B, KT, NTL)                                                                   \
+  hipLaunchKernelGGL((down_wide_kernel<B, KT, NTL, kRowsOut>), grid, blk, 0, stream, aq, sa, w2, s2, \
                      sorted, block_expert, num_padded, expert_offsets, row_scale, slot_out, T, H, I, K1, nullptr, 0)
-#define SRMOE_DOWN_WIDE2(KT) \
-  if (block) SRMOE_DOWN_WIDE(true, KT); else SRMOE_DOWN_WIDE(false, KT);
+#define SRMOE_DOWN_WIDE2(KT)                                   \
+  if (wide) {                                                  \
+    if (block) SRMOE_DOWN_WIDE(true, KT, kDownTilesWide);      \
+    else SRMOE_DOWN_WIDE(false, KT, kDownTilesWide);           \
+  } else {                                                     \
+    if (block) SRMOE_DOWN_WIDE(true, KT, kDownTiles);          \
+    else SRMOE_DOWN_WIDE(false, KT, kDownTiles);               \
+  }
     switch ((I + 63) / 64) {
       case 1: SRMOE_DOWN_WIDE2(1) break;
       case 2: SRMOE_DOWN_WIDE2(2) break;
@@ -772,11 +792,17 @@ hipError_t launch_down_wide_combine(const uint8_t* aq, const float* sa, const ui
   const int nb = (int)(sorted_capacity(T, K1, E1, kTBM) / kTBM);
   const int nbs = (T + kTBM - 1) / kTBM;
   const dim3 blk(256);
-  const dim3 grid(nb * ((H + 128 * kDownTiles - 1) / (128 * kDownTiles)));
+  const bool wide = down_wide_tiles_wide(T, H, K1);
+  const int ntl = wide ? kDownTilesWide : kDownTiles;
+  const dim3 grid(nb * ((H + 128 * ntl - 1) / (128 * ntl)));
   const dim3 grid_c(nbs * ((H + 128 * kCombTiles - 1) / (128 * kCombTiles)));
 #define SRMOE_DOWN_COMB(B, KT)                                                                          \
   do {                                                                                                  \
-    if (parts & 1)                                                                                      \
+    if ((parts & 1) && wide)                                                                            \
+      hipLaunchKernelGGL((down_wide_kernel<B, KT, kDownTilesWide, kBlockedOut>), grid, blk, 0, stream, aq, \
+                         sa, w2, s2, sorted, block_expert, shared_first, expert_offsets, row_scale, slot_out, \
+                         T, H, I, K1, nullptr, 0);                                                      \
+    else if (parts & 1)                                                                                 \
       hipLaunchKernelGGL((down_wide_kernel<B, KT, kDownTiles, kBlockedOut>), grid, blk, 0, stream, aq, sa, \
                          w2, s2, sorted, block_expert, shared_first, expert_offsets, row_scale, slot_out, T, \
                          H, I, K1, nullptr, 0);                                                         \
