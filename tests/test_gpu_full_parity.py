@@ -4,8 +4,10 @@ against the oracle.
 Coverage: every token at decode (64) and prefill (4,096); at the 16k Zipf chunk and the
 unsharded block-scale layer, a token set that puts at least one real row in every row block
 of the sorted layout (every workgroup's tile of rows meets the oracle), plus the hottest
-expert's first and last token. Routing ids, the sorted layout, counts and offsets are
-compared exactly; values per token at 2e-2 (inf-norm relative), with the FP8 tie allowance.
+expert's first and last token. A further case runs every token of a shape large enough for
+the routed down launch's 1,280-column workgroups. Routing ids, the sorted layout, counts and
+offsets are compared exactly; values per token at 2e-2 (inf-norm relative), with the FP8 tie
+allowance.
 The oracle is the unchanged plain definition (intelliparadigm, section 2.1; Optimizing
 GLM4-MoE for production, section 1).
 """
@@ -17,7 +19,7 @@ import torch
 
 import oracle
 from tests.gpu_util import (note, to_dev, bf16_dev, bf16_to_np, make_layer, x_f32, check_rows_with_ties,
-                            token_rel_err, generate_cached)
+                            small_cfg, token_rel_err, generate_cached)
 from workloads import CONFIGS, generate
 
 pytestmark = pytest.mark.gpu
@@ -90,3 +92,28 @@ def test_layer_forward_full_size(name):
     full = layer.out.float()
     assert torch.isfinite(full).all()
     assert (full.abs().amax(dim=1) > 0).all()
+
+
+def test_layer_forward_wide_routed_down_every_token():
+    """The routed experts' down launch at 1,280 columns per workgroup, which moe_layer_forward
+    takes once the routed row blocks give at least 2,048 workgroups at that width, against the
+    oracle on every token. H = 128 keeps the oracle fast; T * K1 = 262,800 slot rows give 2,053
+    row blocks of 128 in H's one column group. Values per token at 2e-2 with the FP8 tie
+    allowance; routing ids exact."""
+    cfg = small_cfg("wide_down", T=29200, H=128, I=64, E=16, K=8, seed=41)
+    assert cfg.T * (cfg.K + 1) // 128 * ((cfg.H + 1279) // 1280) >= 2048
+    inp = generate(cfg)
+    c = inp.cfg
+    layer, W = make_layer(inp, 128)
+    note("wide routed down: moe_layer_forward bm=128, T=29200, H=128")
+    layer.forward_fused(bf16_dev(inp.x_bf16), to_dev(inp.logits), W, 1.0)
+    torch.cuda.synchronize()
+    ids_ref, w_ref = oracle.route_topk_plus_shared(inp.logits, c.K)
+    assert np.array_equal(layer.topk_ids.cpu().numpy(), ids_ref)
+    t0 = time.time()
+    out_ref = oracle.moe_fused(x_f32(inp), inp.logits, c.K, inp.w13_q, inp.s13, inp.w2_q, inp.s2)
+    out = bf16_to_np(layer.out)
+    e, n_tie = check_rows_with_ties(out, out_ref, inp, [[(t, k) for k in range(c.K1)] for t in range(c.T)],
+                                    ids_ref, w_ref)
+    note(f"wide routed down: every token: max per-token rel err {e:.3e}, tokens on the tie allowance "
+         f"{n_tie} (oracle {time.time() - t0:.1f} s)")
