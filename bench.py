@@ -557,6 +557,11 @@ def main():
         # the prefill half of the metric: the 4,096-token chunk (the pages' input length)
         pre = measure("prefill", args, with_extras=False)
         result["prefill"] = pre
+    # which library ran: its path and the source stamp it was built with (the binding
+    # refuses a library whose stamp differs from the sources in the tree)
+    from shared_routed_expert_amd import _lib
+    result["library"] = {"path": os.path.relpath(_lib.LIB_PATH, ROOT),
+                         "source_hash": _lib.lib.srmoe_source_hash().decode()}
     print(json.dumps(result), flush=True)
 
 

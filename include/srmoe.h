@@ -357,6 +357,11 @@ size_t moe_workspace_bytes(int T, int H, int I, int E1, int K1, int block_m, int
 const char* moe_status_string(int status);
 const char* srmoe_status_string(int status);
 int srmoe_last_hip_error(void); /* hipError_t of this thread's last failed launch, 0 if none */
+/* Build stamp: 16 hex digits of the sha256 over the csrc and include sources the library was
+ * compiled from (shared_routed_expert_amd/build.py, source_hash), or "unstamped" for a build
+ * that did not set it. Static storage, never null. The Python binding refuses to load a
+ * library whose stamp differs from the sources beside it. */
+const char* srmoe_source_hash(void);
 
 #ifdef __cplusplus
 }

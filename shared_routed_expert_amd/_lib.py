@@ -3,7 +3,8 @@
 Every function here has the name of the C entry point it calls and only turns
 torch tensors into device pointers (and the current torch stream into a
 hipStream_t). All computation happens in the library's HIP kernels. If the
-library has not been built the import fails loudly; there is no fallback.
+library has not been built, or was built from other sources than the ones beside
+it, the import fails loudly; there is no fallback.
 """
 from __future__ import annotations
 
@@ -63,11 +64,17 @@ def _load():
         "moe_ffn_workspace_offsets": ([I, I, I, I, I, I, I, P], I),
         "srmoe_status_string": ([I], ctypes.c_char_p),
         "srmoe_last_hip_error": ([], I),
+        "srmoe_source_hash": ([], ctypes.c_char_p),
     }
     for name, (args, res) in sigs.items():
         fn = getattr(lib, name)
         fn.argtypes = args
         fn.restype = res
+    from .build import source_hash
+    stamp, want = lib.srmoe_source_hash().decode(), source_hash()
+    if stamp != want:
+        raise ImportError(f"{LIB_PATH} was built from other sources (stamp {stamp}, sources {want}): "
+                          "rebuild it with `python -m shared_routed_expert_amd.build`")
     return lib
 
 
@@ -80,7 +87,7 @@ EXPORTED = ("moe_route_topk_plus_shared", "moe_align_by_expert", "moe_fused_ffn"
             "moe_route_from_x_workspace_bytes", "moe_layer_forward_from_x", "moe_sorted_capacity",
             "moe_align_workspace_bytes", "moe_ffn_workspace_bytes", "moe_ffn_workspace_offsets",
             "srmoe_status_string", "srmoe_last_hip_error", "moe_workspace_bytes", "moe_status_string",
-            "moe_layer_forward_staged", "moe_layer_forward_noalloc")
+            "moe_layer_forward_staged", "moe_layer_forward_noalloc", "srmoe_source_hash")
 
 
 def _ptr(t):

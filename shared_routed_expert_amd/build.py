@@ -4,9 +4,14 @@
 
 Each source is compiled to its own object in parallel (every translation unit holds
 its kernels and their host launchers), then the objects are linked into the library.
+The library is stamped with source_hash() of the sources it was built from
+(srmoe_source_hash); the binding refuses a library whose stamp differs from the
+sources beside it.
 """
 from __future__ import annotations
 
+import glob
+import hashlib
 import os
 import subprocess
 import sys
@@ -30,6 +35,19 @@ FLAGS = [
 ]
 
 
+def source_hash() -> str:
+    """First 16 hex digits of the sha256 over every csrc/*.hip, csrc/*.hpp and include/*.h
+    file (sorted by path relative to the repository root; each path, then its bytes)."""
+    files = sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.hpp"))
+                   + glob.glob(os.path.join(ROOT, "include", "*.h")))
+    h = hashlib.sha256()
+    for f in sorted(files, key=lambda f: os.path.relpath(f, ROOT)):
+        h.update(os.path.relpath(f, ROOT).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
 def _run(cmd):
     r = subprocess.run(cmd, capture_output=True, text=True)
     msgs = "\n".join(l for l in (r.stdout + r.stderr).splitlines()
@@ -39,12 +57,13 @@ def _run(cmd):
 
 def build(verbose: bool = False) -> str:
     os.makedirs(OBJ, exist_ok=True)
+    flags = [*FLAGS, f'-DSRMOE_SOURCE_HASH="{source_hash()}"']
     jobs = []
     for s in SOURCES:
         obj = os.path.join(OBJ, os.path.splitext(s)[0] + ".o")
-        jobs.append((s, obj, [HIPCC, *FLAGS, "-c", os.path.join(CSRC, s), "-o", obj]))
+        jobs.append((s, obj, [HIPCC, *flags, "-c", os.path.join(CSRC, s), "-o", obj]))
     if verbose:
-        print(f"{HIPCC} {' '.join(FLAGS)} -c <each of {', '.join(SOURCES)}>", flush=True)
+        print(f"{HIPCC} {' '.join(flags)} -c <each of {', '.join(SOURCES)}>", flush=True)
     workers = max(1, min(len(jobs), int(os.environ.get("MAX_JOBS", os.cpu_count() or 1))))
     with ThreadPoolExecutor(workers) as pool:
         results = list(pool.map(lambda j: (j[0], *_run(j[2])), jobs))

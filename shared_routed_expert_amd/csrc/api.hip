@@ -165,6 +165,11 @@ const char* moe_status_string(int status) { return srmoe_status_string(status); 
 
 int srmoe_last_hip_error(void) { return g_last_hip_error; }
 
+#ifndef SRMOE_SOURCE_HASH
+#define SRMOE_SOURCE_HASH "unstamped"
+#endif
+const char* srmoe_source_hash(void) { return SRMOE_SOURCE_HASH; }
+
 size_t moe_workspace_bytes(int T, int H, int I, int E1, int K1, int block_m, int scale_mode) {
   const size_t f = moe_ffn_workspace_bytes(T, H, I, E1, K1, block_m, scale_mode);
   if (f == 0) return 0;

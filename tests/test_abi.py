@@ -385,3 +385,18 @@ def test_noalloc_rejects_sizes_beyond_the_array(L):
     assert L.lib.moe_layer_forward_noalloc(*args, 0, 64, 5120, 192, 160, 8, 1.0, 48, FAKE, None) == -2
     assert L.lib.moe_layer_forward_noalloc(*args, 0, 64, 5120, 192, 160, 8, 1.0, 16, 0x10004, None) == -1
     assert L.lib.moe_layer_forward_noalloc(*args, 0, 0, 5120, 192, 160, 8, 1.0, 16, None, None) == 0
+
+
+def test_library_stamp_matches_the_sources(L):
+    """The library reports the hash of the sources it was built from, and that is the hash
+    of the sources in the tree (the binding refuses to load it otherwise)."""
+    from shared_routed_expert_amd.build import source_hash
+    assert L.lib.srmoe_source_hash().decode() == source_hash()
+
+
+def test_a_library_from_other_sources_is_refused(L, monkeypatch):
+    """A stale build fails loudly at load instead of running old kernels."""
+    from shared_routed_expert_amd import build as b
+    monkeypatch.setattr(b, "source_hash", lambda: "0000000000000000")
+    with pytest.raises(ImportError, match="other sources"):
+        L._load()
