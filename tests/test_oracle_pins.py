@@ -212,7 +212,9 @@ def test_router_logits_one_hot_rows():
 
 @pytest.mark.parametrize("name", ["tiny", "prefill16k_zipf"])
 def test_router_logits_reproduce_the_workload_logits(name):
-    """The workloads' logits are the router gate of their x and router weight, rounded to fp32."""
+    """Consistency of the input recipe, not a pin: the workloads' logits are the oracle's router
+    gate of their x and router weight, rounded to fp32 (router_logits itself is pinned by the
+    brute-force and one-hot tests above)."""
     cfg = CONFIGS[name]
     if name != "tiny":
         cfg = cfg.replace(T=64)
