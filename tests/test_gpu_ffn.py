@@ -29,6 +29,11 @@ SMALL = {
     "k_equals_e": small_cfg("k_equals_e", T=33, H=128, I=32, E=8, K=8, seed=14),
     "block": small_cfg("block", T=50, H=384, I=256, E=6, K=2, mode="block128", seed=15),
     "block_ragged": small_cfg("block_ragged", T=131, H=640, I=384, E=9, K=3, mode="block128", seed=16),
+    # an expert's gate/up weights above 2 MB (2 * I * H): the 128-row gate_up tiles take the
+    # expert-grouped order, here with two row blocks per expert
+    "grouped_order": small_cfg("grouped_order", T=400, H=1024, I=1152, E=4, K=2, seed=17),
+    "grouped_order_block": small_cfg("grouped_order_block", T=400, H=1024, I=1152, E=4, K=2, mode="block128",
+                                     seed=18),
     # degenerate routing: no routed slot (the layer is the shared FFN), one routed expert
     "shared_only": small_cfg("shared_only", T=37, H=256, I=64, E=6, K=0, seed=31),
     "one_routed": small_cfg("one_routed", T=29, H=256, I=64, E=1, K=1, seed=32),
